@@ -1,0 +1,206 @@
+/*
+ * tq.h -- C ABI of the rotated-basis ternary projection library (libtq.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes.  Activations are rotated by the signed blockwise
+ * Walsh-Hadamard transform H(D.x)/sqrt(1024) and then multiplied by a ternary
+ * weight matrix stored as row-split planes (base / high / fp16 scale) with one
+ * scale per 128-weight group.  Sources (page title, section):
+ *   [ninfer-skill]   "ninfer 三元制品：容器格式与几何" (ninfer ternary artifact:
+ *                    container format and geometry): §1 alignment constants,
+ *                    §2 ternary formats, §3 row-split geometry, §6 constants.
+ *   [gguf-explainer] "GGUF 完整讲解": §4.3 2-bit code semantics.
+ *   [ninfer-v3]      "artifact-container.md": §6.1 formats, §6.2 layouts,
+ *                    §8 hadamard_signs, §11 error ownership.
+ *   [tensorsharp]    "从 TensorSharp 视角解读 Ternary Bonsai 2 27B": §4.2
+ *                    transform contract, §4.4 network flow, §5.1 rejection
+ *                    policy.
+ *
+ * Conventions shared by every entry point:
+ *  - All sizes are int64_t / uint64_t element or byte counts; leading
+ *    dimensions (ld*) are in elements and must be >= the row width.
+ *  - Pointers named host_* are host memory; all others are device memory
+ *    allocated and owned by the caller.  The library allocates nothing, keeps
+ *    no pointer after returning, and never frees caller memory.
+ *  - Device entry points enqueue work on `stream` (a hipStream_t; NULL means
+ *    the legacy null stream) and return immediately; the caller keeps every
+ *    buffer alive until that work has completed.
+ *  - Validation is synchronous and complete before anything is launched: on
+ *    any status other than TQ_OK nothing was enqueued and tq_last_error()
+ *    returns a message naming the offending argument ("reject rather than
+ *    run wrong": [tensorsharp] §4.2, §5.1; [ninfer-v3] §11.3).
+ *  - Kernels read the stored planes in place (no repacking at run time,
+ *    [ninfer-v3] §7.3) and do not check codes: a PQ2_0 code 3 decodes as +2
+ *    and an out-of-range PTQ1_0 byte decodes by the digit arithmetic;
+ *    tq_unpack_rowsplit reports both.
+ *  - Every output element is written by exactly one thread in a fixed
+ *    order, so results are bitwise reproducible for a given build and shape.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_ARG = 1,          /* null pointer, bad enum, bad leading dimension */
+  TQ_ERR_FORMAT = 2,       /* unknown numeric format                        */
+  TQ_ERR_GEOMETRY = 3,     /* payload size does not match the layout        */
+  TQ_ERR_ALIGN = 4,        /* pointer alignment requirement not met         */
+  TQ_ERR_SHAPE = 5,        /* n, k, rows, batch or count out of range       */
+  TQ_ERR_UNSUPPORTED = 6,  /* valid request this library does not implement */
+  TQ_ERR_DEVICE = 7,       /* the HIP runtime reported an error             */
+  TQ_ERR_DATA = 8          /* host data outside the format's value set      */
+} tq_status;
+
+/* Ternary formats, numbered by their GGUF tensor type ids ([ninfer-skill]
+ * §6: T_PQ2_0 = 142, T_PTQ1_0 = 143).
+ *  PQ2_0_G128:  32 base bytes + 0 high bytes + 2 scale bytes per group of
+ *               128 weights ([ninfer-skill] §2).  Weight j of a group is the
+ *               2-bit code at base byte j/4, bits 2*(j%4), value code-1
+ *               ([gguf-explainer] §4.3).
+ *  PTQ1_0_G128: 24 base + 2 high + 2 scale bytes per group ([ninfer-skill]
+ *               §2).  The pages do not give the trit order; this library's
+ *               convention: u = trit+1; base byte b (0..23) holds trits
+ *               5b..5b+4 as sum u_i*3^i; high byte h (0..1) holds trits
+ *               120+4h..123+4h as sum u_i*3^i.                            */
+typedef enum { TQ_PQ2_0_G128 = 142, TQ_PTQ1_0_G128 = 143 } tq_format;
+
+/* Element types of activations and outputs. */
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+/* The 16-field row-split geometry, in the field order of [ninfer-skill] §3.
+ * k_pad = align_up(k,128); groups_per_row = k_pad/128; per-row plane bytes
+ * are groups times the per-group bytes (2 for the scale); base_offset = 0;
+ * high_offset = align_up(base_bytes,256); scale_offset = high_offset +
+ * align_up(high_bytes,256); payload_bytes = scale_offset + scale_bytes.
+ * Planes are row-major over (row, group); scales are little-endian binary16. */
+typedef struct {
+  uint64_t n, k, k_pad, groups_per_row, base_bytes_per_group,
+      high_bytes_per_group, base_row_bytes, high_row_bytes, scale_row_bytes,
+      base_offset, base_bytes, high_offset, high_bytes, scale_offset,
+      scale_bytes, payload_bytes;
+} tq_geometry;
+
+/* Message for the last non-OK status returned on the calling thread
+ * (thread-local; valid until the next call on that thread). */
+const char *tq_last_error(void);
+
+/* Library version string ("major.minor.patch"). */
+const char *tq_version(void);
+
+/* ----------------------------------------------------------- host ----- */
+
+/* Fill *out with the geometry of an [n, k] matrix ([ninfer-skill] §3).
+ * Errors: TQ_ERR_FORMAT for an unknown format, TQ_ERR_SHAPE unless n,k >= 1,
+ * TQ_ERR_ARG for a null `out`. */
+tq_status tq_geometry_get(int32_t format, int64_t n, int64_t k,
+                          tq_geometry *out);
+
+/* Host packer: encode host_trits (int8 row-major [n][k], values in
+ * {-1,0,1}) and host_scale_bits (binary16 bit patterns, row-major
+ * [n][groups_per_row]) into the row-split payload host_payload, which must
+ * hold exactly payload_bytes = geometry.payload_bytes bytes.  Writes every
+ * byte (inter-plane padding and trits past k up to k_pad are zero trits).
+ * Errors: TQ_ERR_GEOMETRY when payload_bytes differs from the layout size
+ * ("stores N bytes; layout requires M", [ninfer-skill] §1), TQ_ERR_DATA when
+ * a trit lies outside {-1,0,1} (nothing is written then). */
+tq_status tq_pack_rowsplit(int32_t format, int64_t n, int64_t k,
+                           const int8_t *host_trits,
+                           const uint16_t *host_scale_bits,
+                           uint8_t *host_payload, uint64_t payload_bytes);
+
+/* Host unpacker (inverse of tq_pack_rowsplit): host_values int8 [n][k_pad]
+ * receives code-1 for PQ2_0 (so -1..2) and the decoded digit-1 for PTQ1_0;
+ * host_scale_bits [n][groups_per_row] receives the stored binary16 bits.
+ * *host_bad_codes (may be NULL) receives the number of stored codes that are
+ * not ternary (PQ2_0 code 3, PTQ1_0 base byte > 242 or high byte > 80);
+ * the decode is still written.  Errors as for tq_pack_rowsplit. */
+tq_status tq_unpack_rowsplit(int32_t format, int64_t n, int64_t k,
+                             const uint8_t *host_payload,
+                             uint64_t payload_bytes, int8_t *host_values,
+                             uint16_t *host_scale_bits,
+                             uint64_t *host_bad_codes);
+
+/* --------------------------------------------------------- device ----- */
+
+/* Signed blockwise Walsh-Hadamard transform of `rows` rows of width k
+ * ([tensorsharp] §4.2; [ninfer-v3] §8 hadamard_signs):
+ *   inverse == 0:  y_b = H (d_b . x_b) / 32     (projection inputs, head)
+ *   inverse == 1:  y_b = d_b . (H x_b) / 32     (embedding rows)
+ * for every 1024-element block b, with H the unnormalised Sylvester
+ * Hadamard matrix (natural order, H[i][j] = (-1)^popcount(i&j)) and d the
+ * bf16 sign table `signs_bf16` [k] (each entry +1 or -1; only the sign bit
+ * is used).  x: x_dtype (F32, BF16 or F16) row-major with leading dimension
+ * ldx; y: y_dtype (F32, BF16 or F16, rounded to nearest even from the fp32
+ * result) with leading dimension ldy.  rows == 0 is a no-op.
+ * Requirements: k % 1024 == 0 (TQ_ERR_SHAPE), x/y 16-byte aligned and
+ * ldx, ldy multiples of 8 (TQ_ERR_ALIGN), ldx, ldy >= k (TQ_ERR_ARG);
+ * x and y must not overlap unless they are the same buffer with the same
+ * dtype and leading dimension (in-place). */
+tq_status tq_hadamard_signed(const void *x, int32_t x_dtype, int64_t rows,
+                             int64_t k, int64_t ldx,
+                             const uint16_t *signs_bf16, int32_t inverse,
+                             void *y, int32_t y_dtype, int64_t ldy,
+                             void *stream);
+
+/* Decode GEMV: y[b][n] = sum_g s[n][g] * sum_{j in g} t[n][j] * xrot[b][j]
+ * for b < batch, n < N, over the row-split payload (`payload`, exactly
+ * payload_bytes bytes, 256-byte aligned).  xrot: already-rotated
+ * activations, x_dtype F32, BF16 or F16, row-major [batch][ldx]; the kernel
+ * rounds them to binary16 and accumulates in fp32 (finite |xrot| <= 65504).
+ * y: fp32 row-major [batch][ldy].
+ * Requirements: k % 128 == 0, 1 <= batch <= 8, k <= 65536 (PQ2_0) or
+ * k <= 32768 (PTQ1_0) (TQ_ERR_SHAPE); xrot 16-byte aligned, ldx a multiple
+ * of 8 (TQ_ERR_ALIGN); ldx >= k, ldy >= n. */
+tq_status tq_gemv_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
+                           int32_t format, int64_t n, int64_t k,
+                           const void *xrot, int32_t x_dtype, int64_t batch,
+                           int64_t ldx, float *y, int64_t ldy, void *stream);
+
+/* Prefill GEMM: Y[m][n] = sum_g s[n][g] * sum_{j in g} t[n][j] * X[m][j]
+ * for m < M rows of rotated activations X (x_dtype TQ_F16 or TQ_BF16,
+ * row-major [M][ldx], 16-byte aligned, ldx a multiple of 8) against a
+ * PQ2_0_G128 or PTQ1_0_G128 payload, on the matrix cores.  Each weight is
+ * decoded to the binary16 value t*s, which is exact (s is a binary16 and t
+ * is -1, 0 or +1); X is used as binary16 (bf16 input is rounded to binary16,
+ * finite |X| <= 65504); products accumulate in fp32.  Y: y_dtype TQ_F32 or
+ * TQ_BF16, [M][ldy].  M == 0 is a no-op.
+ * Requirements: k % 128 == 0 (TQ_ERR_SHAPE); alignment as above. */
+tq_status tq_gemm_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
+                           int32_t format, int64_t n, int64_t k, const void *x,
+                           int32_t x_dtype, int64_t m, int64_t ldx, void *y,
+                           int32_t y_dtype, int64_t ldy, void *stream);
+
+/* Embedding rows with the inverse transform ([tensorsharp] §4.2, §4.4):
+ * out[i] = per 1024-block d . (H r)/32 where r = dequantised row ids[i] of
+ * the [n, k] payload.  ids: int32 device array [count]; out: fp32
+ * [count][ldo].  An id outside [0, n) produces a zero row and, when
+ * err_word is not NULL, stores 1 into *err_word (device int32, which the
+ * caller zeroes beforehand); nothing outside the payload is read.
+ * Requirements: k % 1024 == 0 (TQ_ERR_SHAPE), ldo >= k, count >= 0. */
+tq_status tq_embed_rows_inverse(const uint8_t *payload, uint64_t payload_bytes,
+                                int32_t format, int64_t n, int64_t k,
+                                const int32_t *ids, int64_t count,
+                                const uint16_t *signs_bf16, float *out,
+                                int64_t ldo, int32_t *err_word, void *stream);
+
+/* Decode hook (for bit-exact checks): for each of `count` row indices in
+ * `rows` (device int32, each in [0, n); others give zero output), write the
+ * decoded values code-1 / digit-1 to values [count][k_pad] (int8) and the
+ * stored scale bits to scale_bits [count][groups_per_row] (uint16). */
+tq_status tq_decode_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
+                             int32_t format, int64_t n, int64_t k,
+                             const int32_t *rows, int64_t count,
+                             int8_t *values, uint16_t *scale_bits,
+                             void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

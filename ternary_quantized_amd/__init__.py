@@ -1,0 +1,246 @@
+"""Python binding of libtq, the MI355X rotated-basis ternary projection library.
+
+Argument marshalling only: every function checks tensor devices, dtypes and
+contiguity, allocates outputs with torch where the C function writes into
+caller memory, and passes raw pointers plus torch's current HIP stream to the
+C ABI declared in ``include/tq.h``.  All computation happens in the HIP
+kernels of ``libtq.so``; if the library is missing, every call raises.
+
+Entry points (same names as the C ABI without the ``tq_`` prefix):
+``geometry``, ``pack_rowsplit``, ``unpack_rowsplit``, ``hadamard_signed``,
+``gemv_rowsplit``, ``gemm_rowsplit``, ``embed_rows_inverse``,
+``decode_rowsplit``.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtq.so")
+
+PQ2_0_G128 = 142
+PTQ1_0_G128 = 143
+FORMATS = {"PQ2_0_G128": PQ2_0_G128, "PTQ1_0_G128": PTQ1_0_G128}
+F32, BF16, F16 = 0, 1, 2
+
+GEOMETRY_FIELDS = (
+    "n", "k", "k_pad", "groups_per_row", "base_bytes_per_group",
+    "high_bytes_per_group", "base_row_bytes", "high_row_bytes",
+    "scale_row_bytes", "base_offset", "base_bytes", "high_offset",
+    "high_bytes", "scale_offset", "scale_bytes", "payload_bytes",
+)
+
+# Exported symbols of include/tq.h.
+EXPORTS = (
+    "tq_last_error", "tq_version", "tq_geometry_get", "tq_pack_rowsplit",
+    "tq_unpack_rowsplit", "tq_hadamard_signed", "tq_gemv_rowsplit",
+    "tq_gemm_rowsplit", "tq_embed_rows_inverse", "tq_decode_rowsplit",
+)
+
+
+class TQError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("tq status %d: %s" % (status, message))
+        self.status = status
+
+
+class Geometry(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_uint64) for f in GEOMETRY_FIELDS]
+
+    def as_dict(self):
+        return {f: int(getattr(self, f)) for f in GEOMETRY_FIELDS}
+
+
+_lib = None
+_i64, _u64, _i32, _vp = ctypes.c_int64, ctypes.c_uint64, ctypes.c_int32, ctypes.c_void_p
+
+
+def lib():
+    """Load libtq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libtq.so is not built (run python -m ternary_quantized_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.tq_last_error.restype = ctypes.c_char_p
+        L.tq_version.restype = ctypes.c_char_p
+        sigs = {
+            "tq_geometry_get": [_i32, _i64, _i64, ctypes.POINTER(Geometry)],
+            "tq_pack_rowsplit": [_i32, _i64, _i64, _vp, _vp, _vp, _u64],
+            "tq_unpack_rowsplit": [_i32, _i64, _i64, _vp, _u64, _vp, _vp, _vp],
+            "tq_hadamard_signed": [_vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _i32, _i64, _vp],
+            "tq_gemv_rowsplit": [_vp, _u64, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _i64, _vp],
+            "tq_gemm_rowsplit": [_vp, _u64, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _i32, _i64, _vp],
+            "tq_embed_rows_inverse": [_vp, _u64, _i32, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp],
+            "tq_decode_rowsplit": [_vp, _u64, _i32, _i64, _i64, _vp, _i64, _vp, _vp, _vp],
+        }
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise TQError(status, lib().tq_last_error().decode())
+
+
+def _fmt(fmt):
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def version():
+    return lib().tq_version().decode()
+
+
+def geometry(fmt, n, k):
+    g = Geometry()
+    _check(lib().tq_geometry_get(_fmt(fmt), n, k, ctypes.byref(g)))
+    return g.as_dict()
+
+
+# ------------------------------------------------------------ host codec ---
+def pack_rowsplit(fmt, trits, scale_bits):
+    """numpy int8 [n, k] trits + uint16 [n, G] fp16 bits -> uint8 payload."""
+    trits = np.ascontiguousarray(trits, dtype=np.int8)
+    scale_bits = np.ascontiguousarray(scale_bits, dtype=np.uint16)
+    n, k = trits.shape
+    g = geometry(fmt, n, k)
+    payload = np.empty(g["payload_bytes"], dtype=np.uint8)
+    _check(lib().tq_pack_rowsplit(_fmt(fmt), n, k, trits.ctypes.data, scale_bits.ctypes.data,
+                                  payload.ctypes.data, payload.size))
+    return payload
+
+
+def unpack_rowsplit(fmt, n, k, payload):
+    """uint8 payload -> (int8 values [n, k_pad], uint16 scale bits, bad codes)."""
+    payload = np.ascontiguousarray(payload, dtype=np.uint8)
+    g = geometry(fmt, n, k)
+    values = np.empty((n, g["k_pad"]), dtype=np.int8)
+    scales = np.empty((n, g["groups_per_row"]), dtype=np.uint16)
+    bad = ctypes.c_uint64(0)
+    _check(lib().tq_unpack_rowsplit(_fmt(fmt), n, k, payload.ctypes.data, payload.size,
+                                    values.ctypes.data, scales.ctypes.data, ctypes.byref(bad)))
+    return values, scales, int(bad.value)
+
+
+# ---------------------------------------------------------------- device ---
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    return {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}[t.dtype]
+
+
+def _dtype_of(code):
+    torch = _torch()
+    return {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16}[code]
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    return t
+
+
+def _signs_ptr(signs):
+    torch = _torch()
+    _dev(signs, "signs")
+    if signs.dtype == torch.bfloat16:
+        return signs.data_ptr()
+    if signs.dtype in (torch.int16, torch.uint16):
+        return signs.data_ptr()
+    raise ValueError("signs must be bf16 (or its int16 bit pattern)")
+
+
+def hadamard_signed(x, signs, inverse=False, out_dtype=None, out=None):
+    """Signed blockwise WHT of the rows of x ([rows, k] device tensor)."""
+    torch = _torch()
+    _dev(x, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D tensor with unit column stride")
+    rows, k = x.shape
+    ycode = _dtype_code(x) if out_dtype is None else {torch.float32: F32, torch.bfloat16: BF16,
+                                                      torch.float16: F16}[out_dtype]
+    if out is None:
+        out = torch.empty((rows, k), dtype=_dtype_of(ycode), device=x.device)
+    _check(lib().tq_hadamard_signed(x.data_ptr(), _dtype_code(x), rows, k, x.stride(0),
+                                    _signs_ptr(signs), int(bool(inverse)), out.data_ptr(), ycode,
+                                    out.stride(0), _stream(x.device)))
+    return out
+
+
+def gemv_rowsplit(payload, fmt, n, k, xrot, out=None):
+    """y [batch, n] fp32 = decode-GEMV of rotated activations xrot [batch, k]."""
+    torch = _torch()
+    _dev(payload, "payload")
+    _dev(xrot, "xrot")
+    if xrot.dim() == 1:
+        xrot = xrot.unsqueeze(0)
+    batch = xrot.shape[0]
+    if out is None:
+        out = torch.empty((batch, n), dtype=torch.float32, device=xrot.device)
+    _check(lib().tq_gemv_rowsplit(payload.data_ptr(), payload.numel() * payload.element_size(),
+                                  _fmt(fmt), n, k, xrot.data_ptr(), _dtype_code(xrot), batch,
+                                  xrot.stride(0), out.data_ptr(), out.stride(0),
+                                  _stream(xrot.device)))
+    return out
+
+
+def gemm_rowsplit(payload, fmt, n, k, x, out_dtype=None, out=None):
+    """Y [m, n] = prefill GEMM of rotated activations x [m, k] (f16 or bf16)."""
+    torch = _torch()
+    _dev(payload, "payload")
+    _dev(x, "x")
+    m = x.shape[0]
+    ycode = F32 if out_dtype in (None, torch.float32) else BF16
+    if out is None:
+        out = torch.empty((m, n), dtype=_dtype_of(ycode), device=x.device)
+    _check(lib().tq_gemm_rowsplit(payload.data_ptr(), payload.numel() * payload.element_size(),
+                                  _fmt(fmt), n, k, x.data_ptr(), _dtype_code(x), m, x.stride(0),
+                                  out.data_ptr(), ycode, out.stride(0), _stream(x.device)))
+    return out
+
+
+def embed_rows_inverse(payload, fmt, n, k, ids, signs, out=None, err_word=None):
+    """out [count, k] fp32: inverse-transformed dequantised rows ids."""
+    torch = _torch()
+    _dev(payload, "payload")
+    _dev(ids, "ids")
+    if ids.dtype != torch.int32:
+        raise ValueError("ids must be int32")
+    count = ids.numel()
+    if out is None:
+        out = torch.empty((count, k), dtype=torch.float32, device=ids.device)
+    err_ptr = None if err_word is None else err_word.data_ptr()
+    _check(lib().tq_embed_rows_inverse(payload.data_ptr(), payload.numel() * payload.element_size(),
+                                       _fmt(fmt), n, k, ids.data_ptr(), count, _signs_ptr(signs),
+                                       out.data_ptr(), out.stride(0) if count else k, err_ptr,
+                                       _stream(ids.device)))
+    return out
+
+
+def decode_rowsplit(payload, fmt, n, k, rows):
+    """(values int8 [count, k_pad], scale bits int16 [count, G]) for rows."""
+    torch = _torch()
+    _dev(payload, "payload")
+    g = geometry(fmt, n, k)
+    count = rows.numel()
+    values = torch.empty((count, g["k_pad"]), dtype=torch.int8, device=rows.device)
+    scales = torch.empty((count, g["groups_per_row"]), dtype=torch.int16, device=rows.device)
+    _check(lib().tq_decode_rowsplit(payload.data_ptr(), payload.numel() * payload.element_size(),
+                                    _fmt(fmt), n, k, rows.data_ptr(), count, values.data_ptr(),
+                                    scales.data_ptr(), _stream(rows.device)))
+    return values, scales

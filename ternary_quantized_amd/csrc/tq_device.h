@@ -1,0 +1,140 @@
+// Device helpers shared by the libtq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+enum { FMT_PQ2 = 142, FMT_PTQ1 = 143 };
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t b) {
+  _Float16 h;
+  __builtin_memcpy(&h, &b, 2);
+  return (float)h;
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// fp32 -> binary16 bits (hardware conversion, round to nearest even).
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  _Float16 h = (_Float16)f;
+  uint16_t b;
+  __builtin_memcpy(&b, &h, 2);
+  return b;
+}
+
+template <int DT>
+__device__ __forceinline__ float load_elem(const void *p, int64_t i) {
+  if constexpr (DT == DT_F32) return static_cast<const float *>(p)[i];
+  else if constexpr (DT == DT_BF16) return bf16_to_f32(static_cast<const uint16_t *>(p)[i]);
+  else return f16_to_f32(static_cast<const uint16_t *>(p)[i]);
+}
+
+// Load 16 consecutive elements starting at element i (16-byte aligned).
+template <int DT>
+__device__ __forceinline__ void load16(const void *p, int64_t i, float v[16]) {
+  if constexpr (DT == DT_F32) {
+    const float4 *q = reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float4 t = q[j];
+      v[4 * j] = t.x; v[4 * j + 1] = t.y; v[4 * j + 2] = t.z; v[4 * j + 3] = t.w;
+    }
+  } else {
+    const uint4 *q = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p) + i);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint4 t = q[j];
+      uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint16_t lo = (uint16_t)(w[e] & 0xFFFF), hi = (uint16_t)(w[e] >> 16);
+        if constexpr (DT == DT_BF16) {
+          v[8 * j + 2 * e] = bf16_to_f32(lo);
+          v[8 * j + 2 * e + 1] = bf16_to_f32(hi);
+        } else {
+          v[8 * j + 2 * e] = f16_to_f32(lo);
+          v[8 * j + 2 * e + 1] = f16_to_f32(hi);
+        }
+      }
+    }
+  }
+}
+
+// Store 16 consecutive elements at element i (16-byte aligned).
+template <int DT>
+__device__ __forceinline__ void store16(void *p, int64_t i, const float v[16]) {
+  if constexpr (DT == DT_F32) {
+    float4 *q = reinterpret_cast<float4 *>(static_cast<float *>(p) + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      q[j] = make_float4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3]);
+  } else {
+    uint4 *q = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p) + i);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint32_t lo, hi;
+        if constexpr (DT == DT_BF16) {
+          lo = f32_to_bf16(v[8 * j + 2 * e]);
+          hi = f32_to_bf16(v[8 * j + 2 * e + 1]);
+        } else {
+          lo = f32_to_f16(v[8 * j + 2 * e]);
+          hi = f32_to_f16(v[8 * j + 2 * e + 1]);
+        }
+        w[e] = lo | (hi << 16);
+      }
+      q[j] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// Flip the sign of v where the bf16 sign entry has its sign bit set (exact).
+__device__ __forceinline__ float apply_sign(float v, uint16_t s) {
+  return __uint_as_float(__float_as_uint(v) ^ ((uint32_t)(s & 0x8000u) << 16));
+}
+
+// In-wave Walsh-Hadamard butterfly of one 1024-element block held as 16
+// consecutive elements per lane (element 16*lane + i in v[i]).  Computes the
+// unnormalised Sylvester transform in natural order: stages on index bits
+// 0..3 run inside the lane, bits 4..9 pair lanes lane ^ 1 .. lane ^ 32.
+__device__ __forceinline__ void wht1024_wave(float v[16], int lane) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float p = __shfl_xor(v[i], m, 64);
+      v[i] = upper ? (p - v[i]) : (v[i] + p);
+    }
+  }
+}
+
+}  // namespace tq

@@ -1,0 +1,363 @@
+// Host entry points of libtq: geometry, the host packer/unpacker, argument
+// validation and dispatch to the kernel launchers.
+//
+// Geometry and plane layout: [ninfer-skill] §2 (format parameters), §3
+// (row-split geometry and field order), §1 (256-byte plane alignment,
+// 128-element K alignment).  Code semantics: [gguf-explainer] §4.3 (PQ2_0
+// codes, LSB pair first, value code-1).  PTQ1_0 trit order: this library's
+// radix-3 convention, stated in include/tq.h.
+
+#include "../../include/tq.h"
+#include "tq_launch.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+namespace {
+
+thread_local std::string g_err;
+
+tq_status fail(tq_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+constexpr uint64_t kGroup = 128;
+constexpr uint64_t kPlaneAlign = 256;
+
+struct Fmt {
+  uint64_t base, high;
+  const char *name;
+};
+
+bool format_params(int32_t f, Fmt *out) {
+  if (f == TQ_PQ2_0_G128) {
+    *out = {32, 0, "PQ2_0_G128"};
+    return true;
+  }
+  if (f == TQ_PTQ1_0_G128) {
+    *out = {24, 2, "PTQ1_0_G128"};
+    return true;
+  }
+  return false;
+}
+
+tq_status geometry(int32_t format, int64_t n, int64_t k, tq_geometry *g) {
+  Fmt f;
+  if (!format_params(format, &f))
+    return fail(TQ_ERR_FORMAT, "unknown numeric format: %d", (int)format);
+  if (n < 1 || k < 1)
+    return fail(TQ_ERR_SHAPE, "shape must be rank 2 with positive dimensions "
+                "(got n=%lld, k=%lld)", (long long)n, (long long)k);
+  g->n = (uint64_t)n;
+  g->k = (uint64_t)k;
+  g->k_pad = align_up(g->k, kGroup);
+  g->groups_per_row = g->k_pad / kGroup;
+  g->base_bytes_per_group = f.base;
+  g->high_bytes_per_group = f.high;
+  g->base_row_bytes = g->groups_per_row * f.base;
+  g->high_row_bytes = g->groups_per_row * f.high;
+  g->scale_row_bytes = g->groups_per_row * 2;
+  g->base_offset = 0;
+  g->base_bytes = g->n * g->base_row_bytes;
+  g->high_offset = align_up(g->base_bytes, kPlaneAlign);
+  g->high_bytes = g->n * g->high_row_bytes;
+  g->scale_offset = g->high_offset + align_up(g->high_bytes, kPlaneAlign);
+  g->scale_bytes = g->n * g->scale_row_bytes;
+  g->payload_bytes = g->scale_offset + g->scale_bytes;
+  return TQ_OK;
+}
+
+tq_status check_payload_size(const tq_geometry &g, uint64_t payload_bytes) {
+  if (payload_bytes != g.payload_bytes)
+    return fail(TQ_ERR_GEOMETRY, "payload stores %llu bytes; layout requires %llu",
+                (unsigned long long)payload_bytes,
+                (unsigned long long)g.payload_bytes);
+  return TQ_OK;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool dtype_ok(int32_t d) { return d == TQ_F32 || d == TQ_BF16 || d == TQ_F16; }
+
+tq_status device_status(hipError_t e, const char *what) {
+  if (e != hipSuccess)
+    return fail(TQ_ERR_DEVICE, "%s: HIP error %d (%s)", what, (int)e,
+                hipGetErrorString(e));
+  return TQ_OK;
+}
+
+// Common validation of a device payload and its shape.
+tq_status check_device_payload(const uint8_t *payload, uint64_t payload_bytes,
+                               int32_t format, int64_t n, int64_t k,
+                               tq_geometry *g, tq::Planes *p) {
+  tq_status st = geometry(format, n, k, g);
+  if (st != TQ_OK) return st;
+  if ((st = check_payload_size(*g, payload_bytes)) != TQ_OK) return st;
+  if (!payload) return fail(TQ_ERR_ARG, "payload is NULL");
+  if (!aligned(payload, kPlaneAlign))
+    return fail(TQ_ERR_ALIGN, "payload must be 256-byte aligned (plane alignment)");
+  p->base = payload + g->base_offset;
+  p->high = payload + g->high_offset;
+  p->scale = reinterpret_cast<const uint16_t *>(payload + g->scale_offset);
+  p->n = n;
+  p->k = k;
+  p->groups = (int64_t)g->groups_per_row;
+  p->base_row = (int64_t)g->base_row_bytes;
+  p->high_row = (int64_t)g->high_row_bytes;
+  p->fmt = format;
+  return TQ_OK;
+}
+
+tq_status check_signs(const uint16_t *signs) {
+  if (!signs) return fail(TQ_ERR_ARG, "signs_bf16 is NULL");
+  if (!aligned(signs, 16))
+    return fail(TQ_ERR_ALIGN, "signs_bf16 must be 16-byte aligned");
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tq_last_error(void) { return g_err.c_str(); }
+
+const char *tq_version(void) { return "0.1.0"; }
+
+tq_status tq_geometry_get(int32_t format, int64_t n, int64_t k, tq_geometry *out) {
+  if (!out) return fail(TQ_ERR_ARG, "out is NULL");
+  tq_geometry g;
+  tq_status st = geometry(format, n, k, &g);
+  if (st == TQ_OK) *out = g;
+  return st;
+}
+
+tq_status tq_pack_rowsplit(int32_t format, int64_t n, int64_t k,
+                           const int8_t *trits, const uint16_t *scale_bits,
+                           uint8_t *payload, uint64_t payload_bytes) {
+  tq_geometry g;
+  tq_status st = geometry(format, n, k, &g);
+  if (st != TQ_OK) return st;
+  if ((st = check_payload_size(g, payload_bytes)) != TQ_OK) return st;
+  if (!trits || !scale_bits || !payload)
+    return fail(TQ_ERR_ARG, "host_trits, host_scale_bits and host_payload must be non-NULL");
+  const uint64_t N = g.n, K = g.k, G = g.groups_per_row;
+  for (uint64_t i = 0; i < N * K; ++i) {
+    int8_t t = trits[i];
+    if (t < -1 || t > 1)
+      return fail(TQ_ERR_DATA, "trit %d at row %llu column %llu is not in {-1,0,1}",
+                  (int)t, (unsigned long long)(i / K), (unsigned long long)(i % K));
+  }
+  std::memset(payload, 0, payload_bytes);
+  uint8_t *base = payload + g.base_offset;
+  uint8_t *high = payload + g.high_offset;
+  uint8_t *scale = payload + g.scale_offset;
+  uint8_t u[kGroup];
+  for (uint64_t r = 0; r < N; ++r) {
+    const int8_t *row = trits + r * K;
+    for (uint64_t gi = 0; gi < G; ++gi) {
+      // digits u = trit + 1; columns past k are zero trits (u = 1)
+      for (uint64_t j = 0; j < kGroup; ++j) {
+        uint64_t col = gi * kGroup + j;
+        u[j] = (uint8_t)(col < K ? row[col] + 1 : 1);
+      }
+      uint8_t *b = base + r * g.base_row_bytes + gi * g.base_bytes_per_group;
+      if (format == TQ_PQ2_0_G128) {
+        for (int q = 0; q < 32; ++q)
+          b[q] = (uint8_t)(u[4 * q] | (u[4 * q + 1] << 2) | (u[4 * q + 2] << 4) |
+                           (u[4 * q + 3] << 6));
+      } else {
+        for (int q = 0; q < 24; ++q) {
+          const uint8_t *d = u + 5 * q;
+          b[q] = (uint8_t)(d[0] + 3 * (d[1] + 3 * (d[2] + 3 * (d[3] + 3 * d[4]))));
+        }
+        uint8_t *h = high + r * g.high_row_bytes + gi * g.high_bytes_per_group;
+        for (int q = 0; q < 2; ++q) {
+          const uint8_t *d = u + 120 + 4 * q;
+          h[q] = (uint8_t)(d[0] + 3 * (d[1] + 3 * (d[2] + 3 * d[3])));
+        }
+      }
+      uint16_t s = scale_bits[r * G + gi];
+      uint8_t *sp = scale + r * g.scale_row_bytes + 2 * gi;
+      sp[0] = (uint8_t)(s & 0xFF);
+      sp[1] = (uint8_t)(s >> 8);
+    }
+  }
+  return TQ_OK;
+}
+
+tq_status tq_unpack_rowsplit(int32_t format, int64_t n, int64_t k,
+                             const uint8_t *payload, uint64_t payload_bytes,
+                             int8_t *values, uint16_t *scale_bits,
+                             uint64_t *bad_codes) {
+  tq_geometry g;
+  tq_status st = geometry(format, n, k, &g);
+  if (st != TQ_OK) return st;
+  if ((st = check_payload_size(g, payload_bytes)) != TQ_OK) return st;
+  if (!payload || !values || !scale_bits)
+    return fail(TQ_ERR_ARG, "host_payload, host_values and host_scale_bits must be non-NULL");
+  const uint64_t N = g.n, G = g.groups_per_row, KP = g.k_pad;
+  const uint8_t *base = payload + g.base_offset;
+  const uint8_t *high = payload + g.high_offset;
+  const uint8_t *scale = payload + g.scale_offset;
+  uint64_t bad = 0;
+  for (uint64_t r = 0; r < N; ++r) {
+    for (uint64_t gi = 0; gi < G; ++gi) {
+      int8_t *out = values + r * KP + gi * kGroup;
+      const uint8_t *b = base + r * g.base_row_bytes + gi * g.base_bytes_per_group;
+      if (format == TQ_PQ2_0_G128) {
+        for (int j = 0; j < 128; ++j) {
+          int code = (b[j >> 2] >> (2 * (j & 3))) & 3;
+          bad += code == 3;
+          out[j] = (int8_t)(code - 1);
+        }
+      } else {
+        for (int q = 0; q < 24; ++q) {
+          int v = b[q];
+          bad += v > 242;
+          for (int i = 0; i < 5; ++i, v /= 3) out[5 * q + i] = (int8_t)(v % 3 - 1);
+        }
+        const uint8_t *h = high + r * g.high_row_bytes + gi * g.high_bytes_per_group;
+        for (int q = 0; q < 2; ++q) {
+          int v = h[q];
+          bad += v > 80;
+          for (int i = 0; i < 4; ++i, v /= 3) out[120 + 4 * q + i] = (int8_t)(v % 3 - 1);
+        }
+      }
+      const uint8_t *sp = scale + r * g.scale_row_bytes + 2 * gi;
+      scale_bits[r * G + gi] = (uint16_t)(sp[0] | (sp[1] << 8));
+    }
+  }
+  if (bad_codes) *bad_codes = bad;
+  return TQ_OK;
+}
+
+tq_status tq_hadamard_signed(const void *x, int32_t x_dtype, int64_t rows,
+                             int64_t k, int64_t ldx, const uint16_t *signs,
+                             int32_t inverse, void *y, int32_t y_dtype,
+                             int64_t ldy, void *stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype))
+    return fail(TQ_ERR_ARG, "x_dtype/y_dtype must be TQ_F32, TQ_BF16 or TQ_F16");
+  if (inverse != 0 && inverse != 1) return fail(TQ_ERR_ARG, "inverse must be 0 or 1");
+  if (rows < 0) return fail(TQ_ERR_SHAPE, "rows must be >= 0");
+  if (k < 1 || k % 1024)
+    return fail(TQ_ERR_SHAPE, "k=%lld: the transform needs a positive multiple of the "
+                "1024-element Hadamard block", (long long)k);
+  if (ldx < k || ldy < k) return fail(TQ_ERR_ARG, "ldx and ldy must be >= k");
+  tq_status st = check_signs(signs);
+  if (st != TQ_OK) return st;
+  if (rows == 0) return TQ_OK;
+  if (!x || !y) return fail(TQ_ERR_ARG, "x and y must be non-NULL");
+  if (!aligned(x, 16) || !aligned(y, 16) || ldx % 8 || ldy % 8)
+    return fail(TQ_ERR_ALIGN, "x and y must be 16-byte aligned with ldx, ldy multiples of 8");
+  if (x == y && (x_dtype != y_dtype || ldx != ldy))
+    return fail(TQ_ERR_ARG, "in-place transform needs equal dtypes and leading dimensions");
+  return device_status(tq::launch_hadamard(x, x_dtype, rows, k, ldx, signs, inverse,
+                                           y, y_dtype, ldy, (hipStream_t)stream),
+                       "tq_hadamard_signed");
+}
+
+tq_status tq_gemv_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
+                           int32_t format, int64_t n, int64_t k, const void *xrot,
+                           int32_t x_dtype, int64_t batch, int64_t ldx, float *y,
+                           int64_t ldy, void *stream) {
+  tq_geometry g;
+  tq::Planes p;
+  tq_status st = check_device_payload(payload, payload_bytes, format, n, k, &g, &p);
+  if (st != TQ_OK) return st;
+  if (k % 128)
+    return fail(TQ_ERR_SHAPE, "k=%lld: device projections need k %% 128 == 0", (long long)k);
+  if (batch < 1 || batch > 8) return fail(TQ_ERR_SHAPE, "batch=%lld must be in 1..8", (long long)batch);
+  if (k > tq::gemv_max_k(format))
+    return fail(TQ_ERR_SHAPE, "k=%lld exceeds the GEMV limit %lld for this format", (long long)k,
+                (long long)tq::gemv_max_k(format));
+  if (!dtype_ok(x_dtype)) return fail(TQ_ERR_ARG, "x_dtype must be TQ_F32, TQ_BF16 or TQ_F16");
+  if (!xrot || !y) return fail(TQ_ERR_ARG, "xrot and y must be non-NULL");
+  if (ldx < k || ldy < n) return fail(TQ_ERR_ARG, "ldx must be >= k and ldy >= n");
+  if (!aligned(xrot, 16) || ldx % 8)
+    return fail(TQ_ERR_ALIGN, "xrot must be 16-byte aligned with ldx a multiple of 8");
+  if (!aligned(y, 4)) return fail(TQ_ERR_ALIGN, "y must be 4-byte aligned");
+  return device_status(tq::launch_gemv(p, xrot, x_dtype, batch, ldx, y, ldy,
+                                       (hipStream_t)stream),
+                       "tq_gemv_rowsplit");
+}
+
+tq_status tq_gemm_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
+                           int32_t format, int64_t n, int64_t k, const void *x,
+                           int32_t x_dtype, int64_t m, int64_t ldx, void *y,
+                           int32_t y_dtype, int64_t ldy, void *stream) {
+  tq_geometry g;
+  tq::Planes p;
+  tq_status st = check_device_payload(payload, payload_bytes, format, n, k, &g, &p);
+  if (st != TQ_OK) return st;
+  if (k % 128)
+    return fail(TQ_ERR_SHAPE, "k=%lld: device projections need k %% 128 == 0", (long long)k);
+  if (m < 0) return fail(TQ_ERR_SHAPE, "m must be >= 0");
+  if (x_dtype != TQ_F16 && x_dtype != TQ_BF16)
+    return fail(TQ_ERR_ARG, "x_dtype must be TQ_F16 or TQ_BF16");
+  if (y_dtype != TQ_F32 && y_dtype != TQ_BF16)
+    return fail(TQ_ERR_ARG, "y_dtype must be TQ_F32 or TQ_BF16");
+  if (m == 0) return TQ_OK;
+  if (!x || !y) return fail(TQ_ERR_ARG, "x and y must be non-NULL");
+  if (ldx < k || ldy < n) return fail(TQ_ERR_ARG, "ldx must be >= k and ldy >= n");
+  if (!aligned(x, 16) || ldx % 8)
+    return fail(TQ_ERR_ALIGN, "x must be 16-byte aligned with ldx a multiple of 8");
+  if (!aligned(y, 4)) return fail(TQ_ERR_ALIGN, "y must be 4-byte aligned");
+  return device_status(tq::launch_gemm(p, static_cast<const uint16_t *>(x), x_dtype, m, ldx, y,
+                                       y_dtype, ldy, (hipStream_t)stream),
+                       "tq_gemm_rowsplit");
+}
+
+tq_status tq_embed_rows_inverse(const uint8_t *payload, uint64_t payload_bytes,
+                                int32_t format, int64_t n, int64_t k,
+                                const int32_t *ids, int64_t count,
+                                const uint16_t *signs, float *out, int64_t ldo,
+                                int32_t *err_word, void *stream) {
+  tq_geometry g;
+  tq::Planes p;
+  tq_status st = check_device_payload(payload, payload_bytes, format, n, k, &g, &p);
+  if (st != TQ_OK) return st;
+  if (k % 1024)
+    return fail(TQ_ERR_SHAPE, "k=%lld: the inverse transform needs a multiple of the "
+                "1024-element Hadamard block", (long long)k);
+  if (count < 0) return fail(TQ_ERR_SHAPE, "count must be >= 0");
+  if ((st = check_signs(signs)) != TQ_OK) return st;
+  if (count == 0) return TQ_OK;
+  if (!ids || !out) return fail(TQ_ERR_ARG, "ids and out must be non-NULL");
+  if (ldo < k) return fail(TQ_ERR_ARG, "ldo must be >= k");
+  if (!aligned(out, 16) || ldo % 4)
+    return fail(TQ_ERR_ALIGN, "out must be 16-byte aligned with ldo a multiple of 4");
+  return device_status(tq::launch_embed(p, ids, count, signs, out, ldo, err_word,
+                                        (hipStream_t)stream),
+                       "tq_embed_rows_inverse");
+}
+
+tq_status tq_decode_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
+                             int32_t format, int64_t n, int64_t k,
+                             const int32_t *rows, int64_t count, int8_t *values,
+                             uint16_t *scale_bits, void *stream) {
+  tq_geometry g;
+  tq::Planes p;
+  tq_status st = check_device_payload(payload, payload_bytes, format, n, k, &g, &p);
+  if (st != TQ_OK) return st;
+  if (count < 0) return fail(TQ_ERR_SHAPE, "count must be >= 0");
+  if (count == 0) return TQ_OK;
+  if (!rows || !values || !scale_bits)
+    return fail(TQ_ERR_ARG, "rows, values and scale_bits must be non-NULL");
+  return device_status(tq::launch_decode(p, rows, count, values, scale_bits,
+                                         (int64_t)g.k_pad, (hipStream_t)stream),
+                       "tq_decode_rowsplit");
+}
+
+}  // extern "C"

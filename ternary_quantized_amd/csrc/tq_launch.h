@@ -1,0 +1,45 @@
+// Internal interface between the host entry points (tq_host.cpp) and the
+// kernel launchers (*.hip).  Launchers assume fully validated arguments and
+// only enqueue work; they return the HIP status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+// Plane geometry in the form the kernels consume (byte offsets into the
+// payload and per-row strides).
+struct Planes {
+  const uint8_t *base;    // payload + base_offset
+  const uint8_t *high;    // payload + high_offset (may be empty)
+  const uint16_t *scale;  // payload + scale_offset, [n][groups]
+  int64_t n, k, groups;
+  int64_t base_row, high_row;  // bytes per row
+  int fmt;                     // 142 or 143
+};
+
+hipError_t launch_hadamard(const void *x, int x_dtype, int64_t rows, int64_t k,
+                           int64_t ldx, const uint16_t *signs, int inverse,
+                           void *y, int y_dtype, int64_t ldy,
+                           hipStream_t stream);
+
+hipError_t launch_gemv(const Planes &p, const void *x, int x_dtype,
+                       int64_t batch, int64_t ldx, float *y, int64_t ldy,
+                       hipStream_t stream);
+
+hipError_t launch_gemm(const Planes &p, const uint16_t *x, int x_dtype,
+                       int64_t m, int64_t ldx, void *y, int y_dtype,
+                       int64_t ldy, hipStream_t stream);
+
+int64_t gemv_max_k(int fmt);
+
+hipError_t launch_embed(const Planes &p, const int32_t *ids, int64_t count,
+                        const uint16_t *signs, float *out, int64_t ldo,
+                        int32_t *err_word, hipStream_t stream);
+
+hipError_t launch_decode(const Planes &p, const int32_t *rows, int64_t count,
+                         int8_t *values, uint16_t *scale_bits, int64_t k_pad,
+                         hipStream_t stream);
+
+}  // namespace tq
