@@ -1,0 +1,317 @@
+"""Benchmark of the rotated-basis ternary projection on one MI355X.
+
+A step is one pass of the decode hot path over one batch of synthetic input:
+the signed Walsh-Hadamard transform of a bf16 activation row (K = 5120,
+output binary16) followed by the PQ2_0_G128 decode GEMV against the
+17408 x 5120 FFN gate/up weight planes.  Inputs are resident in HBM before
+the timed region.  Each step uses the next of 24 distinct weight copies
+(24 x 23.7 MB, more than twice the 256 MB Infinity Cache) so the weight
+stream comes from HBM, and the steps are launched as one HIP graph so the
+host launch rate does not limit them.
+
+Printed: one JSON line with the step throughput (algorithmic GB/s), the
+roofline of the dominant kernel (the GEMV: algorithmic bytes per launch over
+its mean launch time from HIP events on its stream), the oracle's CPU
+throughput on a bounded sample, and secondary figures for the other
+workloads (PTQ1_0 down projection at batch 1/4/8, the vocabulary head and
+embedding rows, and the prefill GEMM in TFLOP/s).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16/bf16 matrix peak
+INFINITY_CACHE = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=240)
+    ap.add_argument("--warmup", type=int, default=24)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-secondary", action="store_true", help="skip configs 3-5")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def copies_for(nbytes, minimum=2):
+    return max(minimum, -(-2 * INFINITY_CACHE // nbytes))
+
+
+def event_timed(torch, fn, launches):
+    """Mean duration (s) of fn(i) over `launches` calls, each bracketed by HIP
+    events on the current stream."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
+    for i in range(launches):
+        starts[i].record()
+        fn(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return float(np.mean(ms)) / 1e3, float(np.median(ms)) / 1e3
+
+
+def load_counters(name, source):
+    """HBM traffic from committed rocprofv3 counter runs, or None when the
+    kernel source changed since they were taken."""
+    path = os.path.join(HERE, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = open(os.path.join(HERE, "ternary_quantized_amd", "csrc", source), "rb").read()
+    if rec.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the projection path here is single-device "
+              "(multi-GPU sharding is a design note, not implemented); use --gpus 1",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import ternary_quantized_amd as tq
+    import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def bits_dev(a, dtype):
+        return to_dev(np.asarray(a, np.uint16).view(np.int16)).view(dtype)
+
+    # ------------------------------------------------------ config 2 step
+    c2 = synth.make_config(2)
+    fmt, n, k = c2["fmt"], c2["n"], c2["k"]
+    payload = tq.pack_rowsplit(fmt, c2["trits"], c2["scale_bits"])
+    plane_bytes = payload.size
+    ncopy = copies_for(plane_bytes)
+    base = to_dev(payload)
+    copies = [base.clone() for _ in range(ncopy)]
+    x = bits_dev(c2["x"], torch.bfloat16)
+    signs = bits_dev(c2["sign_bits"], torch.bfloat16)
+    xrot = torch.empty((1, k), dtype=torch.float16, device=dev)
+    y = torch.empty((1, n), dtype=torch.float32, device=dev)
+
+    def step(i):
+        tq.hadamard_signed(x, signs, out=xrot)
+        tq.gemv_rowsplit(copies[i % ncopy], fmt, n, k, xrot, out=y)
+
+    # algorithmic bytes of a step: planes + x (bf16) + signs (bf16) + y (fp32)
+    step_bytes = plane_bytes + 2 * k + 2 * k + 4 * n
+    # of one GEMV launch: planes + x' (binary16) + y
+    gemv_bytes = plane_bytes + 2 * k + 4 * n
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(ncopy):
+            step(i)
+    torch.cuda.synchronize()
+
+    def capture(nsteps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(nsteps):
+                step(i)
+        return g
+
+    g_warm = capture(max(1, args.warmup))
+    g_timed = capture(args.steps)
+    torch.cuda.synchronize()
+    if args.warmup > 0:
+        g_warm.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g_timed.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = step_bytes * args.steps / elapsed / 1e9
+
+    # correctness spot check of the last step against the library's own
+    # first computation (same weights, same input): bitwise equal
+    y_graph = y.clone()
+    step((args.steps - 1) % ncopy)
+    torch.cuda.synchronize()
+    if not torch.equal(y_graph, y):
+        print("bench: graph replay result differs from eager result", file=sys.stderr)
+        return 1
+
+    # ---------------------------------------- roofline of the GEMV kernel
+    with torch.cuda.stream(stream):
+        tq.hadamard_signed(x, signs, out=xrot)
+        launches = 8 * ncopy
+        gemv_mean, gemv_median = event_timed(
+            torch, lambda i: tq.gemv_rowsplit(copies[i % ncopy], fmt, n, k, xrot, out=y), launches)
+        wht_mean, _ = event_timed(torch, lambda i: tq.hadamard_signed(x, signs, out=xrot), 64)
+    achieved = gemv_bytes / gemv_mean / 1e9
+    counters = load_counters("gemv_pq2_17408x5120_b1_counters.json", "tq_gemv.hip")
+    traffic = None
+    if counters:
+        traffic = counters["hbm_bytes_per_dispatch"]
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "gemv_kernel<PQ2_0_G128, chunk 64, batch 1>",
+                "bytes_per_launch": gemv_bytes, "mean_launch_us": round(gemv_mean * 1e6, 3),
+                "median_launch_us": round(gemv_median * 1e6, 3), "launches": launches}
+    del copies
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------ secondary workloads
+    secondary = {"wht_k5120_b1_mean_launch_us": round(wht_mean * 1e6, 3)}
+    if not args.no_secondary:
+        secondary.update(bench_secondary(torch, tq, synth, to_dev, bits_dev, stream))
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        secondary["copy_calibration_bytes"] = src.numel()
+
+    # ------------------------------------------------------ CPU baseline
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(c2, step_bytes)
+
+    out = {
+        "metric": "ternary GEMV achieved HBM GB/s (% of peak) + prefill GEMM TFLOP/s, 1xMI355X",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16xternary->f32",
+        "data": "synthetic (seeded; shapes and value recipes of the 27B model's FFN gate/up "
+                "projection, no real weights)",
+        "config": {"workload": "FFN gate/up decode: signed WHT (K=5120, bf16 in) + PQ2_0_G128 "
+                               "GEMV N=17408 K=5120 batch 1",
+                   "n": n, "k": k, "batch": 1, "format": fmt,
+                   "weight_copies_rotated": ncopy, "step_bytes": step_bytes,
+                   "launch": "hip graph of all timed steps"},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream):
+    res = {}
+    with torch.cuda.stream(stream):
+        # config 3: PTQ1_0 down projection N=5120 K=17408, batch 1/4/8
+        c3 = synth.make_config(3)
+        p3 = tq.pack_rowsplit(c3["fmt"], c3["trits"], c3["scale_bits"])
+        nc = copies_for(p3.size)
+        cps = [to_dev(p3)]
+        cps += [cps[0].clone() for _ in range(nc - 1)]
+        n3, k3 = c3["n"], c3["k"]
+        x3 = bits_dev(c3["x"], torch.bfloat16)
+        s3 = bits_dev(c3["sign_bits"], torch.bfloat16)
+        for b in (1, 4, 8):
+            xr = tq.hadamard_signed(x3[:b], s3, out_dtype=torch.float16)
+            yb = torch.empty((b, n3), dtype=torch.float32, device=xr.device)
+            mean, _ = event_timed(torch, lambda i: tq.gemv_rowsplit(cps[i % nc], c3["fmt"], n3, k3,
+                                                                  xr, out=yb), 4 * nc)
+            byts = p3.size + 2 * b * k3 + 4 * b * n3
+            res["cfg3_ptq1_down_b%d" % b] = {"mean_launch_us": round(mean * 1e6, 3),
+                                             "gbs": round(byts / mean / 1e9, 1),
+                                             "frac_hbm": round(byts / mean / 1e9 / HBM_PEAK_GBS, 4)}
+        del cps
+        torch.cuda.empty_cache()
+
+        # config 4: vocabulary head N=248320 K=5120 batch 1 + 64 embedding rows
+        c4 = synth.make_config(4)
+        p4 = tq.pack_rowsplit(c4["fmt"], c4["trits"], c4["scale_bits"])
+        n4, k4 = c4["n"], c4["k"]
+        del c4["trits"]
+        cps = [to_dev(p4), None]
+        cps[1] = cps[0].clone()
+        x4 = bits_dev(c4["x"], torch.bfloat16)
+        s4 = bits_dev(c4["sign_bits"], torch.bfloat16)
+        xr = tq.hadamard_signed(x4, s4, out_dtype=torch.float16)
+        y4 = torch.empty((1, n4), dtype=torch.float32, device=xr.device)
+        mean, _ = event_timed(torch, lambda i: tq.gemv_rowsplit(cps[i % 2], c4["fmt"], n4, k4, xr,
+                                                              out=y4), 20)
+        byts = p4.size + 2 * k4 + 4 * n4
+        res["cfg4_head_b1"] = {"mean_launch_us": round(mean * 1e6, 3),
+                               "gbs": round(byts / mean / 1e9, 1),
+                               "frac_hbm": round(byts / mean / 1e9 / HBM_PEAK_GBS, 4)}
+        ids = to_dev(c4["ids"])
+        emb = torch.empty((64, k4), dtype=torch.float32, device=xr.device)
+        mean, _ = event_timed(torch, lambda i: tq.embed_rows_inverse(cps[i % 2], c4["fmt"], n4, k4,
+                                                                   ids, s4, out=emb), 20)
+        res["cfg4_embed_64_rows_us"] = round(mean * 1e6, 3)
+        del cps
+        torch.cuda.empty_cache()
+
+        # config 5: prefill 2048 x 5120 -> WHT (binary16 out) -> GEMM N=17408
+        c5 = synth.make_config(5)
+        p5 = to_dev(tq.pack_rowsplit(c5["fmt"], c5["trits"], c5["scale_bits"]))
+        n5, k5 = c5["n"], c5["k"]
+        x5 = bits_dev(c5["x"], torch.bfloat16)
+        s5 = bits_dev(c5["sign_bits"], torch.bfloat16)
+        xr5 = torch.empty((x5.shape[0], k5), dtype=torch.float16, device=x5.device)
+        wmean, _ = event_timed(torch, lambda i: tq.hadamard_signed(x5, s5, out=xr5), 10)
+        y5 = torch.empty((x5.shape[0], n5), dtype=torch.float32, device=x5.device)
+        gmean, gmed = event_timed(torch, lambda i: tq.gemm_rowsplit(p5, c5["fmt"], n5, k5, xr5,
+                                                                  out=y5), 10)
+        flops = 2.0 * x5.shape[0] * n5 * k5
+        res["cfg5_prefill_gemm"] = {"m": int(x5.shape[0]), "n": n5, "k": k5,
+                                    "mean_launch_us": round(gmean * 1e6, 2),
+                                    "tflops": round(flops / gmean / 1e12, 1),
+                                    "mfma_frac": round(flops / gmean / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                                    "wht_2048x5120_us": round(wmean * 1e6, 2),
+                                    "wht_gbs": round(x5.numel() * 4 / wmean / 1e9, 1)}
+    torch.cuda.synchronize()
+    return res
+
+
+def cpu_baseline(c2, step_bytes):
+    """The float64 oracle (test infrastructure) timed on the host on whole
+    config-2 steps: transform + projection of the same inputs, one thread."""
+    from threadpoolctl import threadpool_limits
+    from oracle import codec, projection as P, transform as T
+    payload = codec.pack_rowsplit(c2["fmt"], c2["trits"], c2["scale_bits"])
+    x = T.bf16_bits_to_f64(c2["x"])
+    d = T.bf16_bits_to_f64(c2["sign_bits"])
+    reps, elapsed = 0, 0.0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while reps < 2 or (elapsed < 10.0 and reps < 8):
+            P.projection(c2["fmt"], c2["n"], c2["k"], payload, x, d)
+            reps += 1
+            elapsed = time.perf_counter() - t0
+    return {"value": round(step_bytes * reps / elapsed / 1e9, 5), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d full config-2 steps (float64 transform + projection of all 17408 rows)"
+                      % reps,
+            "seconds_per_step": round(elapsed / reps, 3)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())
