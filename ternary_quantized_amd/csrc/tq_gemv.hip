@@ -38,6 +38,8 @@ __device__ __forceinline__ half2_t cvt_codes(uint32_t v, int sel) {
   }
 }
 
+__device__ __forceinline__ half2_t bits_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+
 __device__ __forceinline__ float dot2(half2_t a, half2_t b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }
@@ -49,47 +51,76 @@ __device__ __forceinline__ half2_t pack_h2(float a, float b) {
   return r;
 }
 
-__device__ __forceinline__ float xload(const void *x, int xd, int64_t i) {
-  if (xd == DT_F32) return static_cast<const float *>(x)[i];
-  if (xd == DT_BF16) return bf16_to_f32(static_cast<const uint16_t *>(x)[i]);
-  return f16_to_f32(static_cast<const uint16_t *>(x)[i]);
+template <int XD>
+__device__ __forceinline__ float xload(const void *x, int64_t i) {
+  return load_elem<XD>(x, i);
 }
 
-// Number of binary16 pairs a lane chunk feeds to v_dot2.
-template <int FMT, int CW>
-struct Chunk {
-  static constexpr int pairs = CW / 2;
+// Raw activation words of one lane chunk, as loaded (no conversion yet).
+template <int FMT, int CW, int XD>
+struct XRaw {
+  // PQ2_0: CW contiguous elements; PTQ1_0: 32 gathered elements.
+  static constexpr int n = FMT == FMT_PQ2 ? (XD == DT_F32 ? CW : CW / 2) : 32;
+  uint32_t w[n];
 };
 
-// Build the activation pairs of one lane chunk in the order the decoder
-// produces weight pairs, and their fp32 sum (of the rounded values).
-template <int FMT, int CW>
-__device__ __forceinline__ float load_x_chunk(const void *x, int xd, int64_t xrow, int64_t c,
-                                              half2_t xp[CW / 2]) {
-  float v[CW];
+template <int FMT, int CW, int XD>
+__device__ __forceinline__ void load_x_raw(const void *x, int64_t xrow, int64_t c,
+                                           XRaw<FMT, CW, XD> &r) {
   if constexpr (FMT == FMT_PQ2) {
-    const int64_t k0 = c * CW;
+    // CW contiguous elements starting at a multiple of 16: 16-byte loads
+    const u32x4 *q;
+    if constexpr (XD == DT_F32)
+      q = reinterpret_cast<const u32x4 *>(static_cast<const float *>(x) + xrow + c * CW);
+    else
+      q = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(x) + xrow + c * CW);
 #pragma unroll
-    for (int i = 0; i < CW; ++i) v[i] = (float)(_Float16)xload(x, xd, xrow + k0 + i);
-    // dword d covers weights 16d..16d+15; pairs (4q,4q+2) then (4q+1,4q+3).
-#pragma unroll
-    for (int d = 0; d < CW / 16; ++d) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        xp[8 * d + 2 * q] = pack_h2(v[16 * d + 4 * q], v[16 * d + 4 * q + 2]);
-        xp[8 * d + 2 * q + 1] = pack_h2(v[16 * d + 4 * q + 1], v[16 * d + 4 * q + 3]);
-      }
+    for (int i = 0; i < XRaw<FMT, CW, XD>::n / 4; ++i) {
+      const u32x4 v = q[i];
+      r.w[4 * i] = v[0]; r.w[4 * i + 1] = v[1]; r.w[4 * i + 2] = v[2]; r.w[4 * i + 3] = v[3];
     }
   } else {
-    // chunk c = 4*g + q: base bytes 6q..6q+5 (trits 30q..30q+29 of group g)
-    // and the high trits 120+2q, 121+2q.
+    // chunk c = 4*g + q: trits 30q..30q+29 and 120+2q, 121+2q of group g
     const int64_t g = c >> 2;
     const int q = (int)(c & 3);
     const int64_t gk = xrow + g * 128;
 #pragma unroll
-    for (int i = 0; i < 30; ++i) v[i] = (float)(_Float16)xload(x, xd, gk + 30 * q + i);
-    v[30] = (float)(_Float16)xload(x, xd, gk + 120 + 2 * q);
-    v[31] = (float)(_Float16)xload(x, xd, gk + 121 + 2 * q);
+    for (int i = 0; i < 32; ++i) {
+      const int64_t e = i < 30 ? gk + 30 * q + i : gk + 120 + 2 * q + (i - 30);
+      if constexpr (XD == DT_F32) r.w[i] = __float_as_uint(static_cast<const float *>(x)[e]);
+      else r.w[i] = static_cast<const uint16_t *>(x)[e];
+    }
+  }
+}
+
+template <int XD>
+__device__ __forceinline__ float x_elem(uint32_t w, int half) {
+  if constexpr (XD == DT_F32) return __uint_as_float(w);
+  const uint16_t b = (uint16_t)(half ? (w >> 16) : (w & 0xFFFF));
+  if constexpr (XD == DT_BF16) return bf16_to_f32(b);
+  else return f16_to_f32(b);
+}
+
+// Activation pairs of one lane chunk in the order the decoder produces
+// weight pairs, and their fp32 sum (of the binary16-rounded values).
+template <int FMT, int CW, int XD>
+__device__ __forceinline__ float convert_x_chunk(const XRaw<FMT, CW, XD> &r, int64_t c,
+                                                 half2_t xp[CW / 2]) {
+  float v[CW];
+#pragma unroll
+  for (int i = 0; i < CW; ++i) {
+    if constexpr (FMT == FMT_PQ2 && XD != DT_F32) v[i] = x_elem<XD>(r.w[i >> 1], i & 1);
+    else v[i] = x_elem<XD>(r.w[i], 0);
+    v[i] = (float)(_Float16)v[i];
+  }
+  if constexpr (FMT == FMT_PQ2) {
+    // dword d covers weights 16d..16d+15; pair e holds weights (e, e+8).
+#pragma unroll
+    for (int d = 0; d < CW / 16; ++d) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xp[8 * d + e] = pack_h2(v[16 * d + e], v[16 * d + e + 8]);
+    }
+  } else {
 #pragma unroll
     for (int pp = 0; pp < 3; ++pp) {
       const int b0 = 10 * pp, b1 = 10 * pp + 5;  // first trit of the byte pair
@@ -112,13 +143,41 @@ template <int FMT, int CW>
 struct Raw {
   uint32_t w[FMT == FMT_PQ2 ? CW / 16 : 2];
   uint32_t h;      // PTQ1_0: the high byte this lane needs
-  uint16_t s;      // scale bits
+  uint32_t s;      // scale bits (kept in a full register: a 16-bit field
+                   // would make every scale load a serialising round trip)
+};
+
+// Plane pointers of one lane chunk in row 0 (advance by the row strides).
+template <int FMT, int CW>
+struct ChunkPtr {
+  const uint8_t *base;    // base bytes of the chunk (PTQ1_0: 4-byte aligned window)
+  const uint8_t *high;    // PTQ1_0: the group's high bytes
+  const uint16_t *scale;  // the chunk's group scale
 };
 
 template <int FMT, int CW>
-__device__ __forceinline__ void load_raw(const Planes &p, int64_t row, int64_t c, Raw<FMT, CW> &r) {
+__device__ __forceinline__ ChunkPtr<FMT, CW> chunk_ptr(const Planes &p, int64_t c) {
+  ChunkPtr<FMT, CW> r;
   if constexpr (FMT == FMT_PQ2) {
-    const uint8_t *b = p.base + row * p.base_row + c * (CW / 4);
+    r.base = p.base + c * (CW / 4);
+    r.high = nullptr;
+    r.scale = p.scale + (c * CW) / 128;
+  } else {
+    const int64_t g = c >> 2;
+    const int q = (int)(c & 3);
+    r.base = p.base + g * 24 + ((6 * q) & ~3);
+    r.high = p.high + g * 2 + (q >> 1);
+    r.scale = p.scale + g;
+  }
+  return r;
+}
+
+// Raw plane bytes of one lane chunk of row `row` (always a valid row).
+template <int FMT, int CW>
+__device__ __forceinline__ void load_raw(const Planes &p, const ChunkPtr<FMT, CW> &cp, int64_t row,
+                                         Raw<FMT, CW> &r) {
+  const uint8_t *b = cp.base + row * p.base_row;
+  if constexpr (FMT == FMT_PQ2) {
     if constexpr (CW == 64) {
       u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(b));
       r.w[0] = t[0]; r.w[1] = t[1]; r.w[2] = t[2]; r.w[3] = t[3];
@@ -128,18 +187,71 @@ __device__ __forceinline__ void load_raw(const Planes &p, int64_t row, int64_t c
     } else {
       r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(b));
     }
-    r.s = p.scale[row * p.groups + (c * CW) / 128];
     r.h = 0;
   } else {
-    const int64_t g = c >> 2;
-    const int q = (int)(c & 3);
-    const uint8_t *gb = p.base + row * p.base_row + g * 24 + ((6 * q) & ~3);
-    r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(gb));
-    r.w[1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(gb + 4));
-    const uint8_t *hb = p.high + row * p.high_row + g * 2;
-    r.h = hb[q >> 1];
-    r.s = p.scale[row * p.groups + g];
+    r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(b));
+    r.w[1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(b + 4));
+    r.h = cp.high[row * p.high_row];
   }
+  r.s = cp.scale[row * p.groups];
+}
+
+// Loader cursor: the plane pointers of one lane chunk at row `row`,
+// advanced by fixed byte strides (no 64-bit multiplies in the loop).  Rows
+// past n load from the last row instead (a valid address) and are masked.
+template <int FMT, int CW>
+struct Cursor {
+  const uint8_t *b, *h;
+  const uint16_t *s;
+  int64_t row;
+  const uint8_t *lb, *lh;  // last row
+  const uint16_t *ls;
+  int64_t sb, sh, ss, srow;  // strides per step
+};
+
+template <int FMT, int CW>
+__device__ __forceinline__ Cursor<FMT, CW> make_cursor(const Planes &p, const ChunkPtr<FMT, CW> &cp,
+                                                      int64_t row, int64_t row_step) {
+  Cursor<FMT, CW> k;
+  k.row = row;
+  k.b = cp.base + row * p.base_row;
+  k.h = cp.high + row * p.high_row;
+  k.s = cp.scale + row * p.groups;
+  k.lb = cp.base + (p.n - 1) * p.base_row;
+  k.lh = cp.high + (p.n - 1) * p.high_row;
+  k.ls = cp.scale + (p.n - 1) * p.groups;
+  k.sb = row_step * p.base_row;
+  k.sh = row_step * p.high_row;
+  k.ss = row_step * p.groups;
+  k.srow = row_step;
+  return k;
+}
+
+template <int FMT, int CW>
+__device__ __forceinline__ void load_next(Cursor<FMT, CW> &k, int64_t n, Raw<FMT, CW> &r) {
+  const bool in = k.row < n;
+  const uint8_t *b = in ? k.b : k.lb;
+  if constexpr (FMT == FMT_PQ2) {
+    if constexpr (CW == 64) {
+      u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(b));
+      r.w[0] = t[0]; r.w[1] = t[1]; r.w[2] = t[2]; r.w[3] = t[3];
+    } else if constexpr (CW == 32) {
+      u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(b));
+      r.w[0] = t[0]; r.w[1] = t[1];
+    } else {
+      r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(b));
+    }
+    r.h = 0;
+  } else {
+    r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(b));
+    r.w[1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(b + 4));
+    r.h = *(in ? k.h : k.lh);
+  }
+  r.s = *(in ? k.s : k.ls);
+  k.b += k.sb;
+  k.h += k.sh;
+  k.s += k.ss;
+  k.row += k.srow;
 }
 
 // sum_j code_j * x_j over one lane chunk (codes 0..2 for ternary data).
@@ -150,21 +262,32 @@ __device__ __forceinline__ void chunk_dot(const Raw<FMT, CW> &r, int64_t c,
 #pragma unroll
   for (int b = 0; b < B; ++b) part[b] = 0.0f;
   if constexpr (FMT == FMT_PQ2) {
+    // A code masked in place into a binary16 with zero exponent is the exact
+    // subnormal code * 4^e * 2^-24 (e = its 2-bit slot, slots 0..4 of each
+    // half); slots 5..7 are shifted down by 10 first.  Products are summed
+    // per slot class in fp32 and rescaled by powers of two at the end.
+    float a[B][5];
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int e = 0; e < 5; ++e) a[b][e] = 0.0f;
 #pragma unroll
     for (int d = 0; d < CW / 16; ++d) {
-      const uint32_t lo = r.w[d] & 0x33333333u;
-      const uint32_t hi = (r.w[d] >> 2) & 0x33333333u;
+      const uint32_t w = r.w[d], w10 = w >> 10;
+      const uint32_t t[8] = {w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u,
+                             w & 0x00C000C0u, w & 0x03000300u, w10 & 0x00030003u,
+                             w10 & 0x000C000Cu, w10 & 0x00300030u};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const half2_t wl = cvt_codes(lo, q);
-        const half2_t wh = cvt_codes(hi, q);
+      for (int e = 0; e < 8; ++e) {
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-          part[b] = dot2(wl, xp[b][8 * d + 2 * q], part[b]);
-          part[b] = dot2(wh, xp[b][8 * d + 2 * q + 1], part[b]);
-        }
+        for (int b = 0; b < B; ++b)
+          a[b][e < 5 ? e : e - 5] = dot2(bits_h2(t[e]), xp[b][8 * d + e], a[b][e < 5 ? e : e - 5]);
       }
     }
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+      part[b] = a[b][0] * 16777216.0f + a[b][1] * 4194304.0f + a[b][2] * 1048576.0f +
+                a[b][3] * 262144.0f + a[b][4] * 65536.0f;
   } else {
     const int q = (int)(c & 3);
     // the lane's 6 base bytes start 0 or 2 bytes into the loaded window
@@ -195,20 +318,45 @@ __device__ __forceinline__ void chunk_dot(const Raw<FMT, CW> &r, int64_t c,
   }
 }
 
-// Launch shape: R teams of cseg threads (cseg = chunks per row rounded up to
-// a 16-lane segment), each thread handling P rows of its team.
-template <int FMT, int CW, int B, int P>
-__global__ __launch_bounds__(1024) void gemv_kernel(Planes p, const void *__restrict__ x, int xd,
-                                                    int64_t batch, int64_t ldx,
-                                                    float *__restrict__ y, int64_t ldy,
-                                                    int chunks, int cseg, int teams) {
+// Sum over the 16 lanes of each DPP row; the total lands in lane 15 of the
+// row (inclusive scan with row_shr 1, 2, 4, 8).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                            0x111, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                            0x112, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                            0x114, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                            0x118, 0xF, 0xF, true));
+  return v;
+}
+
+// Persistent launch: R teams of cseg threads per workgroup (cseg = chunks
+// per row rounded up to a 16-lane segment); a "pass" is R consecutive rows,
+// one per team.  Workgroup w handles passes w, w + G, w + 2G, ... (G = grid
+// size), so the workgroups resident at one time read one compact band of
+// rows.  Each lane keeps its activation chunk in registers for the whole
+// kernel and the weights of the next D passes in flight: after a pass is
+// consumed its ring slot is refilled with the pass D steps ahead.  Every D
+// passes the segment sums are reduced through LDS and written out.
+template <int FMT, int CW, int B, int D, int XD, int LB>
+__global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restrict__ x,
+                                                  int64_t batch, int64_t ldx,
+                                                  float *__restrict__ y, int64_t ldy,
+                                                  int chunks, int cseg, int teams) {
   __shared__ uint32_t lut[FMT == FMT_PTQ1 ? 768 : 1];
-  __shared__ float red[P * B * 64];  // [pass][b][segment], <= 64 segments
+  __shared__ float red[D * B * 64];  // [slot][b][segment], <= 64 segments
+  // activation pairs of every chunk in decode order, plus chunk sums:
+  // staged once per workgroup (teams share chunks)
+  extern __shared__ uint32_t xlds[];  // [chunk][CW/2 pairs], then [chunk] sums (one batch row)
 
   const int t = threadIdx.x;
   const int team = t / cseg;
   const int c = t % cseg;
   const bool active = team < teams && c < chunks;
+  const int64_t npass = (p.n + teams - 1) / teams;
+  const int64_t G = gridDim.x;
 
   if constexpr (FMT == FMT_PTQ1) {
     // Tables mapping a byte v to its radix-3 digits as fp4 nibbles:
@@ -223,94 +371,398 @@ __global__ __launch_bounds__(1024) void gemv_kernel(Planes p, const void *__rest
       lut[256 + v] = low | (d[4] << 20);
       lut[512 + v] = low;
     }
+  }
+  // ---- stage the activations, one batch row at a time: thread i converts
+  // chunk i of row b into LDS; every lane then copies its own chunk's pairs
+  // into registers
+  half2_t xp[B][CW / 2];
+  float xs[B];
+  const int64_t cc = c < chunks ? c : 0;
+  if constexpr (FMT == FMT_PTQ1) __syncthreads();  // tables ready
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    if (b < batch) {
+      for (int i = t; i < chunks; i += blockDim.x) {
+        XRaw<FMT, CW, XD> xr;
+        load_x_raw<FMT, CW, XD>(x, b * ldx, i, xr);
+        half2_t xp1[CW / 2];
+        const float sum = convert_x_chunk<FMT, CW, XD>(xr, i, xp1);
+        uint32_t *dst = xlds + (int64_t)i * (CW / 2);
+#pragma unroll
+        for (int k = 0; k < CW / 2; k += 4)
+          *reinterpret_cast<u32x4 *>(dst + k) = (u32x4){
+              __builtin_bit_cast(uint32_t, xp1[k]), __builtin_bit_cast(uint32_t, xp1[k + 1]),
+              __builtin_bit_cast(uint32_t, xp1[k + 2]), __builtin_bit_cast(uint32_t, xp1[k + 3])};
+        xlds[(int64_t)chunks * (CW / 2) + i] = __float_as_uint(sum);
+      }
+    }
+    __syncthreads();
+    const bool xok = active && b < batch;
+    const uint32_t *src = xlds + cc * (CW / 2);
+#pragma unroll
+    for (int k = 0; k < CW / 2; k += 4) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(src + k);
+      xp[b][k] = bits_h2(xok ? v[0] : 0u);
+      xp[b][k + 1] = bits_h2(xok ? v[1] : 0u);
+      xp[b][k + 2] = bits_h2(xok ? v[2] : 0u);
+      xp[b][k + 3] = bits_h2(xok ? v[3] : 0u);
+    }
+    xs[b] = xok ? __uint_as_float(xlds[(int64_t)chunks * (CW / 2) + cc]) : 0.0f;
     __syncthreads();
   }
 
-  half2_t xp[B][CW / 2];
-  float xs[B];
+  // ---- weight ring: loads are branch-free (idle lanes read chunk 0, rows
+  // past n read the last row) and masked afterwards; pointers advance by
+  // fixed strides
+  const ChunkPtr<FMT, CW> cp = chunk_ptr<FMT, CW>(p, cc);
+  const int64_t row_step = G * teams;  // rows between consecutive passes
+  Cursor<FMT, CW> cur = make_cursor<FMT, CW>(p, cp, (int64_t)blockIdx.x * teams + team, row_step);
+  Raw<FMT, CW> ring[D];
 #pragma unroll
-  for (int b = 0; b < B; ++b) {
-    if (active && b < batch) {
-      xs[b] = load_x_chunk<FMT, CW>(x, xd, b * ldx, c, xp[b]);
-    } else {
-      xs[b] = 0.0f;
+  for (int d = 0; d < D; ++d) {
+    load_next<FMT, CW>(cur, p.n, ring[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int seg = t >> 4;
+  const int segs_per_team = cseg >> 4;
+  int64_t row = (int64_t)blockIdx.x * teams + team;  // row of ring slot 0
+  for (int64_t base = blockIdx.x; base < npass; base += D * G) {
 #pragma unroll
-      for (int i = 0; i < CW / 2; ++i) xp[b][i] = pack_h2(0.0f, 0.0f);
+    for (int d = 0; d < D; ++d) {
+      float part[B];
+      chunk_dot<FMT, CW, B>(ring[d], cc, xp, lut, part);
+      const float s = f16_to_f32((uint16_t)ring[d].s);
+      // refill the slot with the pass D steps ahead
+      load_next<FMT, CW>(cur, p.n, ring[d]);
+      const bool ok = active && row < p.n;
+      row += row_step;
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float v = row16_sum(ok ? s * (part[b] - xs[b]) : 0.0f);
+        if ((t & 15) == 15) red[(d * B + b) * 64 + seg] = v;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    for (int o = t; o < D * teams * B; o += blockDim.x) {
+      const int d = o / (teams * B);
+      const int rem = o % (teams * B);
+      const int tm = rem / B, b = rem % B;
+      const int64_t orow = (base + d * G) * teams + tm;
+      if (orow >= p.n || b >= batch) continue;
+      float sum = 0.0f;
+      const float *rp = red + (d * B + b) * 64 + tm * segs_per_team;
+      for (int sgi = 0; sgi < segs_per_team; ++sgi) sum += rp[sgi];
+      y[b * ldy + orow] = sum;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// PQ2_0 GEMV on the matrix cores (batch 1..4).
+//
+// v_mfma_f32_4x4x4_16b_f16 multiplies 16 independent 4x4x4 blocks; block q of
+// a wave is lanes 4q..4q+3.  Here a block is one activation chunk of 64
+// weights shared by 4 weight rows: lane 4q+j supplies 4 consecutive (in
+// decode order) weights of row j as the B operand and the matching 4
+// activations of batch row j (batch 1: the same row in all four lanes) as
+// the A operand.  Output element [i][j] of a block is then
+// sum_k x_i[k] * w_j[k] over the chunk; with batch 1 every i is the same
+// activation row, so the element at index lane%4 is row (lane%4)'s partial
+// sum whichever way the block's output is laid out over its lanes.
+//
+// Codes are decoded exactly to binary16 trits with full-rate integer ops:
+// OR-ing a code at mantissa bits 2e (e <= 4) into the exponent of 1024
+// gives 1024 + 4^e * code, and one packed fma with (1/4^e, -(1024/4^e + 1))
+// turns that into code - 1 exactly; codes in bits 10..15 are shifted down
+// first.  A dword of 16 codes takes 9 bit operations and 8 packed fmas.
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// (d & mask) | magic in one v_and_or_b32 (magic held in a VGPR: a VOP3
+// instruction takes at most one literal/SGPR operand here).
+__device__ __forceinline__ uint32_t and_or(uint32_t d, uint32_t mask, uint32_t magic_v) {
+  return (d & mask) | magic_v;
+}
+
+// Two masked code pairs -> 4 trits (binary16) for one MFMA B operand.
+// t = 1024 + m*code (exact); fma(t, 1/m, -(1024/m + 1)) = code - 1 (exact).
+__device__ __forceinline__ half4_t trit4(uint32_t ta, uint32_t tb, float inv_ma, float neg_ca,
+                                         float inv_mb, float neg_cb) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t tt = {ta, tb};
+  const half4_t t4 = __builtin_bit_cast(half4_t, tt);
+  const half4_t m4 = {(_Float16)inv_ma, (_Float16)inv_ma, (_Float16)inv_mb, (_Float16)inv_mb};
+  const half4_t c4 = {(_Float16)neg_ca, (_Float16)neg_ca, (_Float16)neg_cb, (_Float16)neg_cb};
+  return __builtin_elementwise_fma(t4, m4, c4);
+}
+
+// 16 codes of dword d -> 4 MFMA B operands; operand h holds the trits of
+// codes (2h, 2h+8, 2h+1, 2h+9).
+__device__ __forceinline__ void decode_pq2_trit4(uint32_t d, uint32_t magic_v, half4_t w[4]) {
+  const uint32_t d10 = d >> 10;
+  w[0] = trit4(and_or(d, 0x00030003u, magic_v), and_or(d, 0x000C000Cu, magic_v),
+               1.0f, -1025.0f, 0.25f, -257.0f);
+  w[1] = trit4(and_or(d, 0x00300030u, magic_v), and_or(d, 0x00C000C0u, magic_v),
+               0.0625f, -65.0f, 0.015625f, -17.0f);
+  w[2] = trit4(and_or(d, 0x03000300u, magic_v), and_or(d10, 0x00030003u, magic_v),
+               0.00390625f, -5.0f, 1.0f, -1025.0f);
+  w[3] = trit4(and_or(d10, 0x000C000Cu, magic_v), and_or(d10, 0x00300030u, magic_v),
+               0.25f, -257.0f, 0.0625f, -65.0f);
+}
+
+// Lane layout: thread t of the workgroup is lane j = t % 4 of block
+// q = t / 4; blocks [team*cpad, team*cpad + chunks) hold the chunks of team
+// `team`, each team covering 4 rows per pass.  cpad = chunks rounded up to a
+// multiple of 4 (whole 16-lane segments).
+template <int P, int XD, bool BATCHED>
+__global__ __launch_bounds__(1024) void gemv_mfma_kernel(Planes p, const void *__restrict__ x,
+                                                         int64_t batch, int64_t ldx,
+                                                         float *__restrict__ y, int64_t ldy,
+                                                         int chunks, int cpad, int teams) {
+  __shared__ float red[P * (BATCHED ? 4 : 1) * 64 * 4];  // [pass][batch][segment][row j]
+  const int t = threadIdx.x;
+  const int j = t & 3;
+  const int q = t >> 2;
+  const int team = q / cpad;
+  const int c = q % cpad;
+  const bool active = team < teams && c < chunks;
+  const int64_t rows_per_pass = 4 * (int64_t)teams;
+  const int64_t row_base = (int64_t)blockIdx.x * rows_per_pass * P + 4 * team + j;
+
+  // ---- weight loads for all P passes (16 bytes = 64 codes per lane)
+  u32x4 raw[P];
+  uint32_t sraw[P];
+  const uint8_t *wp = p.base + row_base * p.base_row + c * 16;
+  const uint16_t *sp = p.scale + row_base * p.groups + (c >> 1);
+  const int64_t wstep = rows_per_pass * p.base_row, sstep = rows_per_pass * p.groups;
+#pragma unroll
+  for (int it = 0; it < P; ++it) {
+    if (active && row_base + it * rows_per_pass < p.n) {
+      raw[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wp + it * wstep));
+      sraw[it] = sp[it * sstep];
     }
   }
 
-  const int64_t row0 = (int64_t)blockIdx.x * teams * P;
-  Raw<FMT, CW> raw[P];
+  // ---- activations of the chunk as the A operand, in decode order:
+  // dword d, pair e = (16d + e, 16d + e + 8); MFMA step (d, h) uses pairs
+  // 2h, 2h+1.  Batched: lane j carries batch row j (zero beyond batch).
+  half4_t xa[16];  // A operand of MFMA step (dword d, h): xa[4d + h]
+  {
+    const int b = BATCHED ? j : 0;
+    const bool xok = active && b < batch;
 #pragma unroll
-  for (int pi = 0; pi < P; ++pi) {
-    const int64_t row = row0 + (int64_t)pi * teams + team;
-    if (active && row < p.n) load_raw<FMT, CW>(p, row, c, raw[pi]);
-  }
-  float acc[P][B];
+    for (int d = 0; d < 4; ++d) {
+      float v[16];
+      if (xok) {
+        load16<XD>(x, b * ldx + (int64_t)c * 64 + 16 * d, v);
+      } else {
 #pragma unroll
-  for (int pi = 0; pi < P; ++pi) {
-    const int64_t row = row0 + (int64_t)pi * teams + team;
-    float part[B];
-    if (active && row < p.n) {
-      chunk_dot<FMT, CW, B>(raw[pi], c, xp, lut, part);
-      const float s = f16_to_f32(raw[pi].s);
+        for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+      }
 #pragma unroll
-      for (int b = 0; b < B; ++b) acc[pi][b] = s * (part[b] - xs[b]);
-    } else {
-#pragma unroll
-      for (int b = 0; b < B; ++b) acc[pi][b] = 0.0f;
+      for (int h = 0; h < 4; ++h) {
+        const int e = 2 * h;
+        xa[4 * d + h] = (half4_t){(_Float16)v[e], (_Float16)v[e + 8], (_Float16)v[e + 1],
+                                  (_Float16)v[e + 9]};
+      }
     }
   }
+  uint32_t magic_v = 0x64006400u;
+  asm volatile("" : "+v"(magic_v));
 
-  // Reduce within 16-lane segments, then across the team's segments.
   const int seg = t >> 4;
 #pragma unroll
-  for (int pi = 0; pi < P; ++pi) {
+  for (int it = 0; it < P; ++it) {
+    const bool ok = active && row_base + it * rows_per_pass < p.n;
+    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float s = 0.0f;
+    if (ok) {
+      const uint32_t dw[4] = {raw[it][0], raw[it][1], raw[it][2], raw[it][3]};
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      float v = acc[pi][b];
-      v += __shfl_xor(v, 8, 64);
-      v += __shfl_xor(v, 4, 64);
-      v += __shfl_xor(v, 2, 64);
-      v += __shfl_xor(v, 1, 64);
-      if ((t & 15) == 0) red[(pi * B + b) * 64 + seg] = v;
+      for (int d = 0; d < 4; ++d) {
+        half4_t w[4];
+        decode_pq2_trit4(dw[d], magic_v, w);
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          acc = __builtin_amdgcn_mfma_f32_4x4x4f16(xa[4 * d + h], w[h], acc, 0, 0, 0);
+      }
+      s = f16_to_f32(sraw[it]);
+    }
+    // batch 1: element j is row j's partial; batched: lane j of the block
+    // holds its column's four batch rows (elements) -- reduced below per
+    // element.
+    if constexpr (!BATCHED) {
+      float v = j == 0 ? acc[0] : j == 1 ? acc[1] : j == 2 ? acc[2] : acc[3];
+      v *= s;
+      // sum the 4 blocks of this 16-lane segment (lanes with equal j)
+      v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF, true));
+      v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF, true));
+      if ((t & 15) >= 12) red[(it * 64 + seg) * 4 + j] = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = acc[e] * s;
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF, true));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                           0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF, true));
+        acc[e] = v;
+      }
+      // lane 12+j holds (batch e, row j) sums of its segment; stash them
+      if ((t & 15) >= 12) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[((it * 4 + e) * 64 + seg) * 4 + j] = acc[e];
+      }
     }
   }
   __syncthreads();
-  const int segs_per_team = cseg >> 4;
-  for (int o = t; o < P * teams * B; o += blockDim.x) {
-    const int pi = o / (teams * B);
-    const int rem = o % (teams * B);
-    const int tm = rem / B, b = rem % B;
-    const int64_t row = row0 + (int64_t)pi * teams + tm;
+  const int segs = cpad >> 2;
+  const int nb = BATCHED ? 4 : 1;
+  for (int o = t; o < P * teams * 4 * nb; o += blockDim.x) {
+    const int jj = o & 3;
+    const int rest = o >> 2;
+    const int b = rest % nb;
+    const int tm = (rest / nb) % teams;
+    const int it = rest / (nb * teams);
+    const int64_t row = (int64_t)blockIdx.x * rows_per_pass * P + it * rows_per_pass + 4 * tm + jj;
     if (row >= p.n || b >= batch) continue;
+    const float *rp = BATCHED ? red + ((it * 4 + b) * 64 + tm * segs) * 4 + jj
+                              : red + (it * 64 + tm * segs) * 4 + jj;
     float sum = 0.0f;
-    const float *rp = red + (pi * B + b) * 64 + tm * segs_per_team;
-    for (int sgi = 0; sgi < segs_per_team; ++sgi) sum += rp[sgi];
+    for (int sgi = 0; sgi < segs; ++sgi) sum += rp[4 * sgi];
     y[b * ldy + row] = sum;
   }
 }
 
-template <int FMT, int CW, int B, int P>
+// Teams per workgroup: fewest idle lanes, then the smallest workgroup.
+// Workgroups stay within 512 lanes whenever one team fits, so the kernel
+// can be compiled for a 512-lane bound (more registers per lane).
+static int pick_teams(int cseg) {
+  int best_r = 1;
+  double best_eff = -1.0;
+  const int cap = cseg <= 512 ? 512 : 1024;
+  for (int r = 1; r * cseg <= cap; ++r) {
+    const int threads = (r * cseg + 63) / 64 * 64;
+    if (threads > cap) break;
+    const double eff = (double)(r * cseg) / threads;
+    if (eff > best_eff + 1e-9) { best_eff = eff; best_r = r; }
+  }
+  return best_r;
+}
+
+// Resident workgroups per compute unit for a kernel instance (cached).
+template <typename K>
+static int resident_per_cu(K kernel, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1)
+    n = 1;
+  return n;
+}
+
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+template <int FMT, int CW, int B, int D, int XD, int LB>
+static hipError_t gemv_launch(const Planes &p, const void *x, int64_t batch, int64_t ldx, float *y,
+                              int64_t ldy, int chunks, int cseg, int teams, int threads,
+                              hipStream_t st) {
+  auto kern = gemv_kernel<FMT, CW, B, D, XD, LB>;
+  const size_t lds = (size_t)chunks * (CW / 2 + 1) * 4;
+  const int64_t npass = (p.n + teams - 1) / teams;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  const int64_t slots = (int64_t)device_cus() * per_cu;
+  const int64_t grid = npass < slots ? npass : slots;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(threads), lds, st, p, x, batch, ldx, y, ldy,
+                     chunks, cseg, teams);
+  return hipGetLastError();
+}
+
+template <int FMT, int CW, int B, int D>
 static hipError_t gemv_go(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx,
                           float *y, int64_t ldy, hipStream_t st) {
   const int chunks = (int)(p.k / CW);
   const int cseg = (chunks + 15) / 16 * 16;
-  // teams per workgroup: fewest idle lanes, then the smallest workgroup
-  int best_r = 1;
-  double best_eff = -1.0;
-  for (int r = 1; r * cseg <= 1024; ++r) {
-    const int threads = (r * cseg + 63) / 64 * 64;
-    const double eff = (double)(r * cseg) / threads;
-    if (eff > best_eff + 1e-9) { best_eff = eff; best_r = r; }
-    if (r * cseg >= 640) break;
+  const int teams = pick_teams(cseg);
+  const int threads = (teams * cseg + 63) / 64 * 64;
+  // a 512-lane bound leaves each lane up to 256 registers
+  if (threads <= 512) {
+    if (xd == DT_F32)
+      return gemv_launch<FMT, CW, B, D, DT_F32, 512>(p, x, batch, ldx, y, ldy, chunks, cseg, teams,
+                                                     threads, st);
+    if (xd == DT_BF16)
+      return gemv_launch<FMT, CW, B, D, DT_BF16, 512>(p, x, batch, ldx, y, ldy, chunks, cseg, teams,
+                                                      threads, st);
+    return gemv_launch<FMT, CW, B, D, DT_F16, 512>(p, x, batch, ldx, y, ldy, chunks, cseg, teams,
+                                                   threads, st);
   }
-  const int threads = (best_r * cseg + 63) / 64 * 64;
-  const int64_t rows_per_wg = (int64_t)best_r * P;
+  if (xd == DT_F32)
+    return gemv_launch<FMT, CW, B, D, DT_F32, 1024>(p, x, batch, ldx, y, ldy, chunks, cseg, teams,
+                                                    threads, st);
+  if (xd == DT_BF16)
+    return gemv_launch<FMT, CW, B, D, DT_BF16, 1024>(p, x, batch, ldx, y, ldy, chunks, cseg, teams,
+                                                     threads, st);
+  return gemv_launch<FMT, CW, B, D, DT_F16, 1024>(p, x, batch, ldx, y, ldy, chunks, cseg, teams,
+                                                  threads, st);
+}
+
+template <int FMT, int CW>
+static hipError_t gemv_b1(const Planes &p, const void *x, int xd, int64_t ldx, float *y,
+                          int64_t ldy, hipStream_t st) {
+  return gemv_go<FMT, CW, 1, 4>(p, x, xd, 1, ldx, y, ldy, st);
+}
+
+template <int P, bool BATCHED>
+static hipError_t gemv_mfma_go(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx,
+                               float *y, int64_t ldy, hipStream_t st) {
+  const int chunks = (int)(p.k / 64);
+  const int cpad = (chunks + 3) / 4 * 4;
+  const int teams = pick_teams(4 * cpad);
+  const int threads = (teams * 4 * cpad + 63) / 64 * 64;
+  const int64_t rows_per_wg = 4LL * teams * P;
   dim3 grid((unsigned)((p.n + rows_per_wg - 1) / rows_per_wg)), block(threads);
-  hipLaunchKernelGGL((gemv_kernel<FMT, CW, B, P>), grid, block, 0, st, p, x, xd, batch, ldx, y,
-                     ldy, chunks, cseg, best_r);
+  if (xd == DT_F32)
+    hipLaunchKernelGGL((gemv_mfma_kernel<P, DT_F32, BATCHED>), grid, block, 0, st, p, x, batch, ldx,
+                       y, ldy, chunks, cpad, teams);
+  else if (xd == DT_BF16)
+    hipLaunchKernelGGL((gemv_mfma_kernel<P, DT_BF16, BATCHED>), grid, block, 0, st, p, x, batch, ldx,
+                       y, ldy, chunks, cpad, teams);
+  else
+    hipLaunchKernelGGL((gemv_mfma_kernel<P, DT_F16, BATCHED>), grid, block, 0, st, p, x, batch, ldx,
+                       y, ldy, chunks, cpad, teams);
   return hipGetLastError();
+}
+
+// PQ2_0 rows of up to 16384 weights run on the matrix cores (a team of
+// 4 * ceil(k/256) * 4 lanes must fit a 1024-lane workgroup).
+static bool gemv_mfma_fits(const Planes &p) { return p.k <= 16384; }
+
+template <bool BATCHED>
+static hipError_t gemv_mfma(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx,
+                            float *y, int64_t ldy, hipStream_t st) {
+  const int cpad = ((int)(p.k / 64) + 3) / 4 * 4;
+  const int64_t passes = (p.n + 4LL * pick_teams(4 * cpad) - 1) / (4LL * pick_teams(4 * cpad));
+  if (passes >= 512 * 8) return gemv_mfma_go<8, BATCHED>(p, x, xd, batch, ldx, y, ldy, st);
+  return gemv_mfma_go<4, BATCHED>(p, x, xd, batch, ldx, y, ldy, st);
 }
 
 // Largest supported k: a team of at most 1024 lanes must cover a row.
@@ -322,17 +774,20 @@ int64_t gemv_max_k(int fmt) { return fmt == FMT_PQ2 ? 64 * 1024 : 32 * 1024; }
 hipError_t launch_gemv(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx,
                        float *y, int64_t ldy, hipStream_t st) {
   if (p.fmt == FMT_PTQ1) {
-    if (batch <= 1) return gemv_go<FMT_PTQ1, 32, 1, 4>(p, x, xd, batch, ldx, y, ldy, st);
+    if (batch <= 1) return gemv_b1<FMT_PTQ1, 32>(p, x, xd, ldx, y, ldy, st);
     if (batch <= 2) return gemv_go<FMT_PTQ1, 32, 2, 4>(p, x, xd, batch, ldx, y, ldy, st);
     if (batch <= 4) return gemv_go<FMT_PTQ1, 32, 4, 2>(p, x, xd, batch, ldx, y, ldy, st);
     return gemv_go<FMT_PTQ1, 32, 8, 1>(p, x, xd, batch, ldx, y, ldy, st);
   }
   // a chunk never spans two groups (64 | 128); wide rows need wider chunks
   const bool wide32 = p.k / 32 > 1024, wide16 = p.k / 16 > 1024;
-  if (batch <= 1 || (wide32 && batch <= 2))
-    return gemv_go<FMT_PQ2, 64, 1, 4>(p, x, xd, batch, ldx, y, ldy, st) ;
+  if (gemv_mfma_fits(p) && batch >= 2 && batch <= 4)
+    return gemv_mfma<true>(p, x, xd, batch, ldx, y, ldy, st);
+  if (batch <= 1 || (wide32 && batch <= 2)) {
+    if (batch <= 1) return gemv_b1<FMT_PQ2, 64>(p, x, xd, ldx, y, ldy, st);
+    return gemv_go<FMT_PQ2, 64, 2, 2>(p, x, xd, batch, ldx, y, ldy, st);
+  }
   if (wide32) {
-    if (batch <= 2) return gemv_go<FMT_PQ2, 64, 2, 2>(p, x, xd, batch, ldx, y, ldy, st);
     if (batch <= 4) return gemv_go<FMT_PQ2, 64, 4, 1>(p, x, xd, batch, ldx, y, ldy, st);
     return gemv_go<FMT_PQ2, 64, 8, 1>(p, x, xd, batch, ldx, y, ldy, st);
   }
