@@ -147,6 +147,20 @@ struct Raw {
                    // would make every scale load a serialising round trip)
 };
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
 // Plane pointers of one lane chunk in row 0 (advance by the row strides).
 template <int FMT, int CW>
 struct ChunkPtr {
@@ -232,9 +246,12 @@ __device__ __forceinline__ void load_next(Cursor<FMT, CW> &k, int64_t n, Raw<FMT
   const bool in = k.row < n;
   const uint8_t *b = in ? k.b : k.lb;
   if constexpr (FMT == FMT_PQ2) {
-    if constexpr (CW == 64) {
-      u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(b));
-      r.w[0] = t[0]; r.w[1] = t[1]; r.w[2] = t[2]; r.w[3] = t[3];
+    if constexpr (CW >= 64) {
+#pragma unroll
+      for (int q = 0; q < CW / 64; ++q) {
+        u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(b) + q);
+        r.w[4 * q] = t[0]; r.w[4 * q + 1] = t[1]; r.w[4 * q + 2] = t[2]; r.w[4 * q + 3] = t[3];
+      }
     } else if constexpr (CW == 32) {
       u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(b));
       r.w[0] = t[0]; r.w[1] = t[1];
@@ -318,6 +335,24 @@ __device__ __forceinline__ void chunk_dot(const Raw<FMT, CW> &r, int64_t c,
   }
 }
 
+// Sum over aligned segments of SEG (8 or 16) lanes inside each DPP row; the
+// total lands in the segment's last lane (inclusive scan with row_shr 1, 2,
+// 4 (, 8): a shift never reaches past the segment start before the partial
+// it pulls already covers that segment only).
+template <int SEG>
+__device__ __forceinline__ float seg_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                            0x111, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                            0x112, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                            0x114, 0xF, 0xF, true));
+  if constexpr (SEG == 16)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                              0x118, 0xF, 0xF, true));
+  return v;
+}
+
 // Sum over the 16 lanes of each DPP row; the total lands in lane 15 of the
 // row (inclusive scan with row_shr 1, 2, 4, 8).
 __device__ __forceinline__ float row16_sum(float v) {
@@ -340,13 +375,13 @@ __device__ __forceinline__ float row16_sum(float v) {
 // kernel and the weights of the next D passes in flight: after a pass is
 // consumed its ring slot is refilled with the pass D steps ahead.  Every D
 // passes the segment sums are reduced through LDS and written out.
-template <int FMT, int CW, int B, int D, int XD, int LB>
+template <int FMT, int CW, int B, int D, int XD, int LB, int SEG>
 __global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restrict__ x,
                                                   int64_t batch, int64_t ldx,
                                                   float *__restrict__ y, int64_t ldy,
                                                   int chunks, int cseg, int teams) {
   __shared__ uint32_t lut[FMT == FMT_PTQ1 ? 768 : 1];
-  __shared__ float red[D * B * 64];  // [slot][b][segment], <= 64 segments
+  __shared__ float red[D * B * (1024 / SEG)];  // [slot][b][segment]
   // activation pairs of every chunk in decode order, plus chunk sums:
   // staged once per workgroup (teams share chunks)
   extern __shared__ uint32_t xlds[];  // [chunk][CW/2 pairs], then [chunk] sums (one batch row)
@@ -426,8 +461,9 @@ __global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restri
 
   __builtin_amdgcn_sched_barrier(0);
 
-  const int seg = t >> 4;
-  const int segs_per_team = cseg >> 4;
+  constexpr int NSEG = 1024 / SEG;
+  const int seg = t / SEG;
+  const int segs_per_team = cseg / SEG;
   int64_t row = (int64_t)blockIdx.x * teams + team;  // row of ring slot 0
   for (int64_t base = blockIdx.x; base < npass; base += D * G) {
 #pragma unroll
@@ -441,8 +477,8 @@ __global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restri
       row += row_step;
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        const float v = row16_sum(ok ? s * (part[b] - xs[b]) : 0.0f);
-        if ((t & 15) == 15) red[(d * B + b) * 64 + seg] = v;
+        const float v = seg_sum<SEG>(ok ? s * (part[b] - xs[b]) : 0.0f);
+        if ((t & (SEG - 1)) == SEG - 1) red[(d * B + b) * NSEG + seg] = v;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -454,11 +490,183 @@ __global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restri
       const int64_t orow = (base + d * G) * teams + tm;
       if (orow >= p.n || b >= batch) continue;
       float sum = 0.0f;
-      const float *rp = red + (d * B + b) * 64 + tm * segs_per_team;
+      const float *rp = red + (d * B + b) * NSEG + tm * segs_per_team;
       for (int sgi = 0; sgi < segs_per_team; ++sgi) sum += rp[sgi];
       y[b * ldy + orow] = sum;
     }
     __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// PQ2_0 batch-1 GEMV, one wave per row.
+//
+// A row of k = 1024*m weights is k/4 bytes; lane l of the wave reads, for
+// each of the A = m/4 whole kilobytes of the row, the 16 bytes at
+// 1024*i + 16*l (64 weights, inside group 32*i + l/2) and, for each of the
+// BQ = m%4 remaining 256-byte blocks, the 4 bytes at 1024*A + 256*j + 4*l
+// (16 weights, inside group 32*A + 8*j + l/8).  Every load instruction of the
+// wave covers one contiguous span, the wave's partial sums are reduced with
+// DPP row shifts and four lane reads, and lane 0 writes the row: waves never
+// synchronise, so each is an independent persistent stream over rows
+// gw, gw + W, gw + 2W, ... (W = waves in the grid) with D rows in flight.
+template <int A, int BQ>
+struct WRaw {
+  uint32_t w[4 * A + BQ];
+  uint32_t s[A + BQ];
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v = seg_sum<16>(v);  // lanes 15, 31, 47, 63 hold their row's sum
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 15)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 47)) +
+         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+template <int A, int BQ, int D, int XD>
+__global__ __launch_bounds__(256) void gemv_wave_kernel(Planes p, const void *__restrict__ x,
+                                                        float *__restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t W = (int64_t)gridDim.x * 4;
+  constexpr int NP = A + BQ;  // pieces per lane
+
+  // ---- activation pieces (binary16 pairs: weights (e, e+8) of each dword)
+  half2_t xp[4 * A + BQ][8];
+  float xs[NP];
+  {
+#pragma unroll
+    for (int i = 0; i < A; ++i) {
+      float v[64];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) load16<XD>(x, 4096 * i + 64 * lane + 16 * q, v + 16 * q);
+      float sum = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 64; ++q) { v[q] = (float)(_Float16)v[q]; sum += v[q]; }
+      xs[i] = sum;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xp[4 * i + d][e] = pack_h2(v[16 * d + e], v[16 * d + e + 8]);
+    }
+#pragma unroll
+    for (int j = 0; j < BQ; ++j) {
+      float v[16];
+      load16<XD>(x, 4096 * A + 1024 * j + 16 * lane, v);
+      float sum = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) { v[q] = (float)(_Float16)v[q]; sum += v[q]; }
+      xs[A + j] = sum;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xp[4 * A + j][e] = pack_h2(v[e], v[e + 8]);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- per-lane plane offsets inside a row
+  const uint8_t *b0 = p.base + 16 * lane;
+  const uint8_t *b1 = p.base + 1024 * A + 4 * lane;
+  const uint16_t *s0 = p.scale + lane / 2;
+  const uint16_t *s1 = p.scale + 32 * A + lane / 8;
+  auto load_row = [&](int64_t row, WRaw<A, BQ> &r) {
+    const int64_t rr = row < p.n ? row : p.n - 1;
+    const uint8_t *rb0 = b0 + rr * p.base_row;
+    const uint8_t *rb1 = b1 + rr * p.base_row;
+    const uint16_t *rs0 = s0 + rr * p.groups;
+    const uint16_t *rs1 = s1 + rr * p.groups;
+#pragma unroll
+    for (int i = 0; i < A; ++i) {
+      const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(rb0 + 1024 * i));
+      r.w[4 * i] = t[0]; r.w[4 * i + 1] = t[1]; r.w[4 * i + 2] = t[2]; r.w[4 * i + 3] = t[3];
+      r.s[i] = rs0[32 * i];
+    }
+#pragma unroll
+    for (int j = 0; j < BQ; ++j) {
+      r.w[4 * A + j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(rb1 + 256 * j));
+      r.s[A + j] = rs1[8 * j];
+    }
+  };
+
+  WRaw<A, BQ> ring[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    load_row(gw + d * W, ring[d]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int64_t base = gw; base < p.n; base += D * W) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int64_t row = base + d * W;
+      // sum over the lane's pieces of s * (sum code*x - sum x)
+      float acc = 0.0f;
+#pragma unroll
+      for (int pc = 0; pc < NP; ++pc) {
+        const int nd = pc < A ? 4 : 1;
+        const int d0 = pc < A ? 4 * pc : 4 * A + (pc - A);
+        float a[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int q = 0; q < nd; ++q) {
+          const uint32_t w = ring[d].w[d0 + q], w10 = w >> 10;
+          const uint32_t t[8] = {w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u,
+                                 w & 0x00C000C0u, w & 0x03000300u, w10 & 0x00030003u,
+                                 w10 & 0x000C000Cu, w10 & 0x00300030u};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            a[e < 5 ? e : e - 5] = dot2(bits_h2(t[e]), xp[d0 + q][e], a[e < 5 ? e : e - 5]);
+        }
+        const float cx = a[0] * 16777216.0f + a[1] * 4194304.0f + a[2] * 1048576.0f +
+                         a[3] * 262144.0f + a[4] * 65536.0f;
+        acc += f16_to_f32((uint16_t)ring[d].s[pc]) * (cx - xs[pc]);
+      }
+      // refill the slot with the row D steps ahead
+      load_row(row + D * W, ring[d]);
+      const float tot = wave_sum(acc);
+      if (lane == 0 && row < p.n) y[row] = tot;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <int A, int BQ, int XD>
+static hipError_t gemv_wave_go(const Planes &p, const void *x, float *y, hipStream_t st) {
+  constexpr int D = 8;
+  auto kern = gemv_wave_kernel<A, BQ, D, XD>;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int64_t blocks_needed = (p.n + 3) / 4;
+  const int64_t slots = (int64_t)device_cus() * per_cu;
+  const int64_t grid = blocks_needed < slots ? blocks_needed : slots;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, p, x, y);
+  return hipGetLastError();
+}
+
+template <int A, int BQ>
+static hipError_t gemv_wave_dt(const Planes &p, const void *x, int xd, float *y, hipStream_t st) {
+  if (xd == DT_F32) return gemv_wave_go<A, BQ, DT_F32>(p, x, y, st);
+  if (xd == DT_BF16) return gemv_wave_go<A, BQ, DT_BF16>(p, x, y, st);
+  return gemv_wave_go<A, BQ, DT_F16>(p, x, y, st);
+}
+
+// k = 1024*m with m <= 11: pieces A = m/4 kilobytes + BQ = m%4 blocks.
+static bool gemv_wave_fits(const Planes &p) {
+  return p.fmt == FMT_PQ2 && p.k % 1024 == 0 && p.k / 1024 >= 1 && p.k / 1024 <= 11;
+}
+
+static hipError_t gemv_wave(const Planes &p, const void *x, int xd, float *y, hipStream_t st) {
+  switch (p.k / 1024) {
+    case 1: return gemv_wave_dt<0, 1>(p, x, xd, y, st);
+    case 2: return gemv_wave_dt<0, 2>(p, x, xd, y, st);
+    case 3: return gemv_wave_dt<0, 3>(p, x, xd, y, st);
+    case 4: return gemv_wave_dt<1, 0>(p, x, xd, y, st);
+    case 5: return gemv_wave_dt<1, 1>(p, x, xd, y, st);
+    case 6: return gemv_wave_dt<1, 2>(p, x, xd, y, st);
+    case 7: return gemv_wave_dt<1, 3>(p, x, xd, y, st);
+    case 8: return gemv_wave_dt<2, 0>(p, x, xd, y, st);
+    case 9: return gemv_wave_dt<2, 1>(p, x, xd, y, st);
+    case 10: return gemv_wave_dt<2, 2>(p, x, xd, y, st);
+    default: return gemv_wave_dt<2, 3>(p, x, xd, y, st);
   }
 }
 
@@ -666,24 +874,12 @@ static int resident_per_cu(K kernel, int threads) {
   return n;
 }
 
-static int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cus[dev]) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1)
-      v = 256;
-    cus[dev] = v;
-  }
-  return cus[dev];
-}
 
-template <int FMT, int CW, int B, int D, int XD, int LB>
+template <int FMT, int CW, int B, int D, int XD, int LB, int SEG>
 static hipError_t gemv_launch(const Planes &p, const void *x, int64_t batch, int64_t ldx, float *y,
                               int64_t ldy, int chunks, int cseg, int teams, int threads,
                               hipStream_t st) {
-  auto kern = gemv_kernel<FMT, CW, B, D, XD, LB>;
+  auto kern = gemv_kernel<FMT, CW, B, D, XD, LB, SEG>;
   const size_t lds = (size_t)chunks * (CW / 2 + 1) * 4;
   const int64_t npass = (p.n + teams - 1) / teams;
   int per_cu = 0;
@@ -697,37 +893,43 @@ static hipError_t gemv_launch(const Planes &p, const void *x, int64_t batch, int
   return hipGetLastError();
 }
 
-template <int FMT, int CW, int B, int D>
+template <int FMT, int CW, int B, int D, int SEG = 16>
 static hipError_t gemv_go(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx,
                           float *y, int64_t ldy, hipStream_t st) {
   const int chunks = (int)(p.k / CW);
-  const int cseg = (chunks + 15) / 16 * 16;
+  const int cseg = (chunks + SEG - 1) / SEG * SEG;
   const int teams = pick_teams(cseg);
   const int threads = (teams * cseg + 63) / 64 * 64;
   // a 512-lane bound leaves each lane up to 256 registers
   if (threads <= 512) {
     if (xd == DT_F32)
-      return gemv_launch<FMT, CW, B, D, DT_F32, 512>(p, x, batch, ldx, y, ldy, chunks, cseg, teams,
-                                                     threads, st);
+      return gemv_launch<FMT, CW, B, D, DT_F32, 512, SEG>(p, x, batch, ldx, y, ldy, chunks, cseg,
+                                                          teams, threads, st);
     if (xd == DT_BF16)
-      return gemv_launch<FMT, CW, B, D, DT_BF16, 512>(p, x, batch, ldx, y, ldy, chunks, cseg, teams,
-                                                      threads, st);
-    return gemv_launch<FMT, CW, B, D, DT_F16, 512>(p, x, batch, ldx, y, ldy, chunks, cseg, teams,
-                                                   threads, st);
+      return gemv_launch<FMT, CW, B, D, DT_BF16, 512, SEG>(p, x, batch, ldx, y, ldy, chunks, cseg,
+                                                           teams, threads, st);
+    return gemv_launch<FMT, CW, B, D, DT_F16, 512, SEG>(p, x, batch, ldx, y, ldy, chunks, cseg,
+                                                        teams, threads, st);
   }
   if (xd == DT_F32)
-    return gemv_launch<FMT, CW, B, D, DT_F32, 1024>(p, x, batch, ldx, y, ldy, chunks, cseg, teams,
-                                                    threads, st);
+    return gemv_launch<FMT, CW, B, D, DT_F32, 1024, SEG>(p, x, batch, ldx, y, ldy, chunks, cseg,
+                                                         teams, threads, st);
   if (xd == DT_BF16)
-    return gemv_launch<FMT, CW, B, D, DT_BF16, 1024>(p, x, batch, ldx, y, ldy, chunks, cseg, teams,
-                                                     threads, st);
-  return gemv_launch<FMT, CW, B, D, DT_F16, 1024>(p, x, batch, ldx, y, ldy, chunks, cseg, teams,
-                                                  threads, st);
+    return gemv_launch<FMT, CW, B, D, DT_BF16, 1024, SEG>(p, x, batch, ldx, y, ldy, chunks, cseg,
+                                                          teams, threads, st);
+  return gemv_launch<FMT, CW, B, D, DT_F16, 1024, SEG>(p, x, batch, ldx, y, ldy, chunks, cseg,
+                                                       teams, threads, st);
 }
 
 template <int FMT, int CW>
 static hipError_t gemv_b1(const Planes &p, const void *x, int xd, int64_t ldx, float *y,
                           int64_t ldy, hipStream_t st) {
+  // PQ2_0 rows whose 128-weight chunks fill whole 8-lane segments: one lane
+  // streams 32 bytes per row (halves the per-row bookkeeping per weight)
+  if constexpr (FMT == FMT_PQ2) {
+    if ((p.k / 128) % 8 == 0 && p.k / 128 <= 512)
+      return gemv_go<FMT, 128, 1, 4, 8>(p, x, xd, 1, ldx, y, ldy, st);
+  }
   return gemv_go<FMT, CW, 1, 4>(p, x, xd, 1, ldx, y, ldy, st);
 }
 
@@ -783,6 +985,7 @@ hipError_t launch_gemv(const Planes &p, const void *x, int xd, int64_t batch, in
   const bool wide32 = p.k / 32 > 1024, wide16 = p.k / 16 > 1024;
   if (gemv_mfma_fits(p) && batch >= 2 && batch <= 4)
     return gemv_mfma<true>(p, x, xd, batch, ldx, y, ldy, st);
+  if (batch <= 1 && gemv_wave_fits(p)) return gemv_wave(p, x, xd, y, st);
   if (batch <= 1 || (wide32 && batch <= 2)) {
     if (batch <= 1) return gemv_b1<FMT_PQ2, 64>(p, x, xd, ldx, y, ldy, st);
     return gemv_go<FMT_PQ2, 64, 2, 2>(p, x, xd, batch, ldx, y, ldy, st);
