@@ -228,6 +228,310 @@ __global__ __launch_bounds__(256) void gemm_kernel(Planes p, const uint16_t *__r
   }
 }
 
+// ---------------------------------------------------------------------------
+// PQ2_0 prefill GEMM: 512-thread workgroups (8 waves), 64-deep K steps
+// through two LDS stages, one barrier per step.
+//
+// Stage layout: X rows and decoded weight rows of [64 k + 8 pad] binary16.
+// Inside every 16-wide k block both are stored in the k order
+// (0,8,1,9,...,7,15): one dword of 16 codes decodes into the pairs (e, e+8),
+// and X is permuted to match, so an MFMA k slot holds the same k in both
+// operands.  Weights are decoded exactly with full-rate integer ops: the
+// code ORed into the exponent field of 1024 gives 1024 + 4^e*code, one fma
+// turns it into code - 1, and the product with the group scale is exactly 0
+// or +-s.
+//
+// Register ring: while step s is multiplied, register set (s+1)&1 holds
+// step s+1 (decoded and stored into the other stage between step s's MFMA
+// slices) and set s&1 is refilled with step s+2, so each global load has a
+// whole step to land.  The code loads are plain (cached) loads: one 128-byte
+// line of a weight row serves 8 consecutive steps.
+//
+// Two tile shapes share the kernel: 256 x 256 tiles (waves 2 x 4 of 128 x
+// 64) for the bulk, and 128 x 64 sub-tiles (waves 4 x 2 of 32 x 32) for the
+// tiles of a last, partial round, which is split 8 ways so it fills the
+// chip instead of a fraction of it.
+constexpr int G2K = 64, G2ROW = G2K + 8;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t trit_pair_scaled(uint32_t t, float inv_m, float neg_c,
+                                                     half2_t s2) {
+  half2_t a = __builtin_bit_cast(half2_t, t), m, c;
+  m.x = m.y = (_Float16)inv_m;
+  c.x = c.y = (_Float16)neg_c;
+  const half2_t trit = __builtin_elementwise_fma(a, m, c);  // exactly code - 1
+  return __builtin_bit_cast(uint32_t, trit * s2);            // exactly 0 or +-s
+}
+
+// Half of a dword of 16 codes -> 4 binary16 pairs of t*s: part 0 gives the
+// pairs (code e, code e+8) for e = 0..3, part 1 for e = 4..7.
+template <int PART>
+__device__ __forceinline__ void decode_pq2_ts4(uint32_t d, uint32_t magic, half2_t s2,
+                                               uint32_t o[4]) {
+  if constexpr (PART == 0) {
+    o[0] = trit_pair_scaled((d & 0x00030003u) | magic, 1.0f, -1025.0f, s2);
+    o[1] = trit_pair_scaled((d & 0x000C000Cu) | magic, 0.25f, -257.0f, s2);
+    o[2] = trit_pair_scaled((d & 0x00300030u) | magic, 0.0625f, -65.0f, s2);
+    o[3] = trit_pair_scaled((d & 0x00C000C0u) | magic, 0.015625f, -17.0f, s2);
+  } else {
+    const uint32_t d10 = d >> 10;
+    o[0] = trit_pair_scaled((d & 0x03000300u) | magic, 0.00390625f, -5.0f, s2);
+    o[1] = trit_pair_scaled((d10 & 0x00030003u) | magic, 1.0f, -1025.0f, s2);
+    o[2] = trit_pair_scaled((d10 & 0x000C000Cu) | magic, 0.25f, -257.0f, s2);
+    o[3] = trit_pair_scaled((d10 & 0x00300030u) | magic, 0.0625f, -65.0f, s2);
+  }
+}
+
+template <int XD>
+__device__ __forceinline__ uint32_t x_pair_f16(uint32_t v) {
+  if constexpr (XD == DT_BF16) {
+    const uint32_t lo = f32_to_f16(bf16_to_f32((uint16_t)(v & 0xFFFF)));
+    const uint32_t hi = f32_to_f16(bf16_to_f32((uint16_t)(v >> 16)));
+    return lo | (hi << 16);
+  } else {
+    return v;
+  }
+}
+
+// One output tile of TM x TN at (m0, n0): waves WAVES_M x (8 / WAVES_M),
+// each 32*FM x 32*FN.
+template <int XD, int YD, int TM, int TN, int FM, int FN, int WAVES_M>
+__device__ __forceinline__ void gemm_pq2_tile(const Planes &p, const uint16_t *__restrict__ X,
+                                              int64_t M, int64_t ldx, void *__restrict__ Y,
+                                              int64_t ldy, int64_t m0, int64_t n0,
+                                              _Float16 *lds2) {
+  constexpr int WAVES_N = 8 / WAVES_M;
+  static_assert(WAVES_M * 32 * FM == TM && WAVES_N * 32 * FN == TN, "wave grid must cover the tile");
+  constexpr int TPR = 512 / TM;       // threads per X row
+  constexpr int HX = G2K / TPR;       // halves of X per thread and step
+  constexpr int XQ = HX / 8;          // 16-byte X loads (and LDS writes) per thread and step
+  static_assert(HX % 16 == 0 && XQ <= 4, "X share must be whole 16-wide k blocks");
+  constexpr int STAGE = (TM + TN) * G2ROW;
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = (wave / WAVES_N) * 32 * FM, wn = (wave % WAVES_N) * 32 * FN;
+  const int nsteps = (int)(p.k / G2K);  // even: k is a multiple of 128
+
+  // X loads: row xr, halves [HX*xq, HX*xq + HX) of a step
+  const int xr = t / TPR, xq = t % TPR;
+  const bool xrow_ok = m0 + xr < M;
+  const uint16_t *xsrc = X + (xrow_ok ? (m0 + xr) : 0) * ldx + HX * xq;
+  // code loads (threads below 2*TN): row wr, codes [32*wh, 32*wh + 32) of a
+  // step (8 bytes) and that row's group scale
+  const bool wthread = t < 2 * TN;
+  const int wr = wthread ? t >> 1 : 0, wh = t & 1;
+  const bool wrow_ok = wthread && n0 + wr < p.n;
+  const int64_t wrow = wrow_ok ? n0 + wr : 0;
+  const uint8_t *wsrc = p.base + wrow * p.base_row + 8 * wh;
+  const uint16_t *ssrc = p.scale + wrow * p.groups;
+
+  uint32_t xreg[2][HX / 2], wreg[4][2], sreg[4];
+  auto clamp = [&](int st) { return st < nsteps ? st : nsteps - 1; };  // past the end: a harmless re-read
+  auto load_x = [&](int set, int st) {
+    const int64_t k0 = (int64_t)clamp(st) * G2K;
+    const u32x4_t *q = reinterpret_cast<const u32x4_t *>(xsrc + k0);
+#pragma unroll
+    for (int i = 0; i < XQ; ++i) {
+      const u32x4_t v = q[i];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xreg[set][4 * i + c] = v[c];
+    }
+  };
+  auto load_w = [&](int set, int st) {
+    if (wthread) {
+      const int64_t k0 = (int64_t)clamp(st) * G2K;
+      const u32x2_t w = *reinterpret_cast<const u32x2_t *>(wsrc + k0 / 4);
+      wreg[set][0] = w[0];
+      wreg[set][1] = w[1];
+      sreg[set] = ssrc[k0 / 128];
+    }
+  };
+  uint32_t magic = 0x64006400u;
+  asm volatile("" : "+v"(magic));
+  // quarter q of X set `set` and code set `wset` into an LDS stage: one
+  // 16-byte write of permuted X (while q < XQ) and one of 8 decoded weights
+  auto store_piece = [&](int set, int wset, int buf, int q) {
+    _Float16 *As = lds2 + buf * STAGE;
+    _Float16 *Bs = As + TM * G2ROW;
+    if (q < XQ) {
+      const uint32_t *xv = xreg[set] + 8 * (q >> 1) + 2 * (q & 1);
+      uint32_t lo[2], hi[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        lo[c] = xrow_ok ? x_pair_f16<XD>(xv[c]) : 0u;
+        hi[c] = xrow_ok ? x_pair_f16<XD>(xv[4 + c]) : 0u;
+      }
+      u32x4_t xo;
+      xo[0] = __builtin_amdgcn_perm(hi[0], lo[0], 0x05040100u);
+      xo[1] = __builtin_amdgcn_perm(hi[0], lo[0], 0x07060302u);
+      xo[2] = __builtin_amdgcn_perm(hi[1], lo[1], 0x05040100u);
+      xo[3] = __builtin_amdgcn_perm(hi[1], lo[1], 0x07060302u);
+      *reinterpret_cast<u32x4_t *>(As + xr * G2ROW + HX * xq + 8 * q) = xo;
+    }
+    if (wthread) {
+      const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)sreg[wset]);
+      half2_t s2;
+      s2.x = s2.y = wrow_ok ? sh : (_Float16)0.0f;
+      uint32_t o[4];
+      if (q & 1)
+        decode_pq2_ts4<1>(wreg[wset][q >> 1], magic, s2, o);
+      else
+        decode_pq2_ts4<0>(wreg[wset][q >> 1], magic, s2, o);
+      *reinterpret_cast<u32x4_t *>(Bs + wr * G2ROW + 32 * wh + 8 * q) =
+          (u32x4_t){o[0], o[1], o[2], o[3]};
+    }
+  };
+
+  floatx16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  // step s: X set s&1 is refilled with step s+2 and code set s&3 with step
+  // s+4 (both already stored), stage s&1 is multiplied, and between its four
+  // 16-deep k slices step s+1 (X set (s+1)&1, code set (s+1)&3) is stored
+  // into the other stage.  Codes come from HBM, so they are fetched further
+  // ahead; X mostly hits in L2.
+  auto step = [&](int s, int ph) {  // ph = s & 3
+    load_x(ph & 1, s + 2);
+    load_w(ph, s + 4);
+    const int buf = ph & 1;
+    const _Float16 *As = lds2 + buf * STAGE;
+    const _Float16 *Bs = As + TM * G2ROW;
+#pragma unroll
+    for (int ks = 0; ks < G2K / 16; ++ks) {
+      const int kb = ks * 16 + 8 * (lane >> 5);
+      half8_t a[FM], bf[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        a[i] = *reinterpret_cast<const half8_t *>(As + (wm + 32 * i + (lane & 31)) * G2ROW + kb);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bf[j] = *reinterpret_cast<const half8_t *>(Bs + (wn + 32 * j + (lane & 31)) * G2ROW + kb);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bf[j], acc[i][j], 0, 0, 0);
+      store_piece((ph + 1) & 1, (ph + 1) & 3, buf ^ 1, ks);
+    }
+    __syncthreads();
+  };
+
+  load_x(0, 0);
+  load_w(0, 0);
+  load_x(1, 1);
+#pragma unroll
+  for (int i = 1; i < 4; ++i) load_w(i, i);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) store_piece(0, 0, 0, q);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 4) {  // nsteps is even
+    step(s, 0);
+    step(s + 1, 1);
+    if (s + 2 < nsteps) {
+      step(s + 2, 2);
+      step(s + 3, 3);
+    }
+  }
+
+  // epilogue: D[i][j] of a 32x32 block is in lane j + 32*((i/4) % 2),
+  // element 4*(i/8) + i%4
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t col = n0 + wn + 32 * j + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row < M && col < p.n) {
+          if constexpr (YD == DT_F32)
+            static_cast<float *>(Y)[row * ldy + col] = acc[i][j][v];
+          else
+            static_cast<uint16_t *>(Y)[row * ldy + col] = f32_to_bf16(acc[i][j][v]);
+        }
+      }
+    }
+  }
+}
+
+// Work split of one launch over 256 x 256 tiles: workgroups [0, nbig) take
+// whole tiles, the rest take 128 x 64 sub-tiles (8 per tile) of the tiles
+// left over.  With `xcd` set, tiles are numbered band-major and XCD x (the
+// workgroups b with b % 8 == x) owns the contiguous tiles [x*per,
+// (x+1)*per), the first big_per of them whole; otherwise tiles go in plain
+// order.
+struct GemmSplit {
+  int tiles_n;  // 256-wide tiles along N
+  int per;      // tiles per XCD
+  int big_per;  // whole tiles per XCD
+  int nbig;     // workgroups on whole tiles
+  int xcd;
+};
+
+template <int XD, int YD>
+__global__ __launch_bounds__(512) void gemm_pq2_kernel(Planes p, const uint16_t *__restrict__ X,
+                                                       int64_t M, int64_t ldx,
+                                                       void *__restrict__ Y, int64_t ldy,
+                                                       GemmSplit sp) {
+  extern __shared__ __attribute__((aligned(16))) _Float16 lds2[];
+  const int b = blockIdx.x;
+  int tile, sub = -1;
+  if (b < sp.nbig) {
+    tile = sp.xcd ? (b % 8) * sp.per + b / 8 : b;
+  } else {
+    const int r = b - sp.nbig;
+    if (sp.xcd) {
+      const int s2 = r / 8;  // nbig is a multiple of 8, so r % 8 == b % 8
+      tile = (r % 8) * sp.per + sp.big_per + s2 / 8;
+      sub = s2 % 8;
+    } else {
+      tile = sp.nbig + r / 8;
+      sub = r % 8;
+    }
+  }
+  const int64_t m0 = (int64_t)(tile / sp.tiles_n) * 256, n0 = (int64_t)(tile % sp.tiles_n) * 256;
+  if (sub < 0)
+    gemm_pq2_tile<XD, YD, 256, 256, 4, 2, 2>(p, X, M, ldx, Y, ldy, m0, n0, lds2);
+  else
+    gemm_pq2_tile<XD, YD, 128, 64, 1, 1, 4>(p, X, M, ldx, Y, ldy, m0 + 128 * (sub >> 2),
+                                            n0 + 64 * (sub & 3), lds2);
+}
+
+template <int XD, int YD>
+static hipError_t gemm_pq2_go(const Planes &p, const uint16_t *x, int64_t m, int64_t ldx, void *y,
+                              int64_t ldy, hipStream_t st) {
+  GemmSplit sp;
+  sp.tiles_n = (int)((p.n + 255) / 256);
+  const int total = sp.tiles_n * (int)((m + 255) / 256);
+  const int cus = device_cus();
+  // a last round that would occupy at most 1/8 of the CUs is split 8 ways
+  const int left = total % cus;
+  const bool split = total > cus && left > 0 && 8 * left <= cus;
+  sp.xcd = total % 8 == 0 && (!split || left % 8 == 0);
+  if (sp.xcd) {
+    sp.per = total / 8;
+    sp.big_per = split ? sp.per - left / 8 : sp.per;
+    sp.nbig = 8 * sp.big_per;
+  } else {
+    sp.per = sp.big_per = 0;
+    sp.nbig = split ? total - left : total;
+  }
+  const int grid = sp.nbig + 8 * (total - sp.nbig);
+  const size_t lds = (size_t)2 * (256 + 256) * G2ROW * sizeof(_Float16);
+  auto kern = gemm_pq2_kernel<XD, YD>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, p, x, m, ldx, y, ldy, sp);
+  return hipGetLastError();
+}
+
 template <int FMT, int XD>
 static hipError_t gemm_go(const Planes &p, const uint16_t *x, int64_t m, int64_t ldx, void *y,
                           int yd, int64_t ldy, hipStream_t st) {
@@ -245,6 +549,14 @@ static hipError_t gemm_go(const Planes &p, const uint16_t *x, int64_t m, int64_t
 
 hipError_t launch_gemm(const Planes &p, const uint16_t *x, int xd, int64_t m, int64_t ldx, void *y,
                        int yd, int64_t ldy, hipStream_t st) {
+  // PQ2_0 with k a multiple of the 64-deep step: the pipelined 256x256 kernel
+  if (p.fmt == FMT_PQ2 && p.k % G2K == 0) {
+    if (xd == DT_F16)
+      return yd == DT_F32 ? gemm_pq2_go<DT_F16, DT_F32>(p, x, m, ldx, y, ldy, st)
+                          : gemm_pq2_go<DT_F16, DT_BF16>(p, x, m, ldx, y, ldy, st);
+    return yd == DT_F32 ? gemm_pq2_go<DT_BF16, DT_F32>(p, x, m, ldx, y, ldy, st)
+                        : gemm_pq2_go<DT_BF16, DT_BF16>(p, x, m, ldx, y, ldy, st);
+  }
   if (p.fmt == FMT_PQ2)
     return xd == DT_F16 ? gemm_go<FMT_PQ2, DT_F16>(p, x, m, ldx, y, yd, ldy, st)
                         : gemm_go<FMT_PQ2, DT_BF16>(p, x, m, ldx, y, yd, ldy, st);

@@ -148,7 +148,7 @@ struct Raw {
 };
 
 // Compute units of the current device (cached per device).
-static int device_cus() {
+int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

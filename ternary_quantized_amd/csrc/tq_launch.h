@@ -34,6 +34,9 @@ hipError_t launch_gemm(const Planes &p, const uint16_t *x, int x_dtype,
 
 int64_t gemv_max_k(int fmt);
 
+// compute units of the current device (cached per device)
+int device_cus();
+
 hipError_t launch_embed(const Planes &p, const int32_t *ids, int64_t count,
                         const uint16_t *signs, float *out, int64_t ldo,
                         int32_t *err_word, hipStream_t stream);

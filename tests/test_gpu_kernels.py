@@ -201,6 +201,43 @@ def test_gemm_integer_exact_and_matches_gemv():
     assert torch.equal(yv, y[:8])
 
 
+def _cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("case", ["xcd_split", "plain_split", "two_steps"])
+def test_gemm_tail_split_integer_exact(case):
+    """Tile counts just past a whole round of the device: the left-over
+    256 x 256 tiles run as 128 x 64 sub-tiles.  Integer data make every
+    output exact, so any tile or sub-tile mapping slip shows."""
+    cus = _cus()
+    if case == "xcd_split":      # tiles % 8 == 0, left-over tiles % 8 == 0
+        tm = 8
+        tn = (cus + cus // 8) // tm
+        m, n, k = tm * 256 - 37, tn * 256 - 100, 256
+    elif case == "plain_split":  # tile count not a multiple of 8
+        tm = 7
+        tn = -(-(cus + 3) // tm)
+        m, n, k = tm * 256 - 5, tn * 256 - 17, 256
+    else:                        # smallest k: two steps
+        tm = 8
+        tn = (cus + cus // 8) // tm
+        m, n, k = tm * 256, tn * 256, 128
+    rng = np.random.default_rng(len(case))
+    trits = synth.trits_uniform(rng, n, k)
+    sb = np.full((n, k // 128), 0x3C00, np.uint16)
+    payload = dev(torch, tq.pack_rowsplit("PQ2_0_G128", trits, sb))
+    xi = rng.integers(-8, 9, size=(m, k)).astype(np.float16)
+    xd = dev(torch, xi.view(np.uint16).view(np.int16)).view(torch.float16)
+    say("gemm tail split %s m=%d n=%d k=%d cus=%d" % (case, m, n, k, cus))
+    y = tq.gemm_rowsplit(payload, "PQ2_0_G128", n, k, xd)
+    torch.cuda.synchronize()
+    expect = xi.astype(np.float64) @ trits.T.astype(np.float64)  # exact: |sum| <= 2048
+    got = y.cpu().numpy()
+    bad = np.argwhere(got != expect.astype(np.float32))
+    assert bad.size == 0, "first mismatches (row, col): %s" % bad[:5].tolist()
+
+
 # ------------------------------------------------------------- embedding ---
 @pytest.mark.parametrize("fmt", ["PQ2_0_G128", "PTQ1_0_G128"])
 @pytest.mark.parametrize("n,k", [(50, 1024), (300, 5120)])
