@@ -2,16 +2,18 @@
 
 A step is one pass of the decode hot path over one batch of synthetic input:
 the signed Walsh-Hadamard transform of a bf16 activation row (K = 5120,
-output binary16) followed by the PQ2_0_G128 decode GEMV against the
-17408 x 5120 FFN gate/up weight planes.  Inputs are resident in HBM before
-the timed region.  Each step uses the next of 24 distinct weight copies
+rounded to binary16) and the PQ2_0_G128 decode GEMV against the 17408 x 5120
+FFN gate/up weight planes, issued as the library's one-launch decode step
+(tq_rotated_gemv_rowsplit: the transform runs in every workgroup while its
+first weight rows are in flight).  Inputs are resident in HBM before the
+timed region.  Each step uses the next of 24 distinct weight copies
 (24 x 23.7 MB, more than twice the 256 MB Infinity Cache) so the weight
 stream comes from HBM, and the steps are launched as one HIP graph so the
 host launch rate does not limit them.
 
 Printed: one JSON line with the step throughput (algorithmic GB/s), the
-roofline of the dominant kernel (the GEMV: algorithmic bytes per launch over
-its mean launch time from HIP events on its stream), the oracle's CPU
+roofline of the dominant kernel (the fused decode kernel: algorithmic bytes
+per launch over its mean launch time from HIP events on its stream), the oracle's CPU
 throughput on a bounded sample, and secondary figures for the other
 workloads (PTQ1_0 down projection at batch 1/4/8, the vocabulary head and
 embedding rows, and the prefill GEMM in TFLOP/s).
@@ -111,12 +113,16 @@ def main():
     y = torch.empty((1, n), dtype=torch.float32, device=dev)
 
     def step(i):
+        tq.rotated_gemv_rowsplit(copies[i % ncopy], fmt, n, k, x, signs, out=y)
+
+    def step_two_launches(i):
         tq.hadamard_signed(x, signs, out=xrot)
         tq.gemv_rowsplit(copies[i % ncopy], fmt, n, k, xrot, out=y)
 
-    # algorithmic bytes of a step: planes + x (bf16) + signs (bf16) + y (fp32)
+    # algorithmic bytes of a step (one launch): planes + x (bf16) + signs
+    # (bf16) + y (fp32)
     step_bytes = plane_bytes + 2 * k + 2 * k + 4 * n
-    # of one GEMV launch: planes + x' (binary16) + y
+    # of the unfused GEMV launch: planes + x' (binary16) + y
     gemv_bytes = plane_bytes + 2 * k + 4 * n
 
     stream = torch.cuda.Stream()
@@ -154,28 +160,43 @@ def main():
         print("bench: graph replay result differs from eager result", file=sys.stderr)
         return 1
 
-    # ---------------------------------------- roofline of the GEMV kernel
+    # ------------------------------ roofline of the fused decode kernel
     with torch.cuda.stream(stream):
-        tq.hadamard_signed(x, signs, out=xrot)
         launches = 8 * ncopy
-        gemv_mean, gemv_median = event_timed(
+        step_mean, step_median = event_timed(torch, step, launches)
+        # the same step as two launches (transform, then GEMV), for context
+        tq.hadamard_signed(x, signs, out=xrot)
+        gemv_mean, _ = event_timed(
             torch, lambda i: tq.gemv_rowsplit(copies[i % ncopy], fmt, n, k, xrot, out=y), launches)
         wht_mean, _ = event_timed(torch, lambda i: tq.hadamard_signed(x, signs, out=xrot), 64)
-    achieved = gemv_bytes / gemv_mean / 1e9
-    counters = load_counters("gemv_pq2_17408x5120_b1_counters.json", "tq_gemv.hip")
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2, stream=stream):
+            for i in range(args.steps):
+                step_two_launches(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g2.replay()
+        torch.cuda.synchronize()
+        two_launch_us = (time.perf_counter() - t0) * 1e6 / args.steps
+        del g2
+    achieved = step_bytes / step_mean / 1e9
+    counters = load_counters("rotated_gemv_pq2_17408x5120_b1_counters.json", "tq_gemv.hip")
     traffic = None
     if counters:
         traffic = counters["hbm_bytes_per_dispatch"]
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "gemv_kernel<PQ2_0_G128, chunk 64, batch 1>",
-                "bytes_per_launch": gemv_bytes, "mean_launch_us": round(gemv_mean * 1e6, 3),
-                "median_launch_us": round(gemv_median * 1e6, 3), "launches": launches}
+                "kernel": "gemv_wave_kernel<A=1, BQ=1, ring 6, x bf16, fused transform>",
+                "bytes_per_launch": step_bytes, "mean_launch_us": round(step_mean * 1e6, 3),
+                "median_launch_us": round(step_median * 1e6, 3), "launches": launches}
     del copies
     torch.cuda.empty_cache()
 
     # ------------------------------------------------ secondary workloads
-    secondary = {"wht_k5120_b1_mean_launch_us": round(wht_mean * 1e6, 3)}
+    secondary = {"two_launch_step_us": round(two_launch_us, 3),
+                 "wht_k5120_b1_mean_launch_us": round(wht_mean * 1e6, 3),
+                 "gemv_unfused_mean_launch_us": round(gemv_mean * 1e6, 3),
+                 "gemv_unfused_gbs": round(gemv_bytes / gemv_mean / 1e9, 1)}
     if not args.no_secondary:
         secondary.update(bench_secondary(torch, tq, synth, to_dev, bits_dev, stream))
 
@@ -207,7 +228,7 @@ def main():
         "data": "synthetic (seeded; shapes and value recipes of the 27B model's FFN gate/up "
                 "projection, no real weights)",
         "config": {"workload": "FFN gate/up decode: signed WHT (K=5120, bf16 in) + PQ2_0_G128 "
-                               "GEMV N=17408 K=5120 batch 1",
+                               "GEMV N=17408 K=5120 batch 1, one launch",
                    "n": n, "k": k, "batch": 1, "format": fmt,
                    "weight_copies_rotated": ncopy, "step_bytes": step_bytes,
                    "launch": "hip graph of all timed steps"},

@@ -162,6 +162,25 @@ tq_status tq_gemv_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
                            const void *xrot, int32_t x_dtype, int64_t batch,
                            int64_t ldx, float *y, int64_t ldy, void *stream);
 
+/* Decode step in one launch: the signed transform of the projection input
+ * ([tensorsharp] §4.2) fused with the decode GEMV,
+ *   y[b][n] = sum_g s[n][g] * sum_{j in g} t[n][j] * r[b][j],
+ *   r_b = binary16( H (d_b . x_b) / 32 )  per 1024-element block b,
+ * i.e. exactly tq_hadamard_signed (inverse 0, y_dtype F16) followed by
+ * tq_gemv_rowsplit on its output, without the intermediate buffer or the
+ * second launch.  x: unrotated activations, x_dtype F32, BF16 or F16,
+ * row-major [batch][ldx]; signs_bf16 [k] as for tq_hadamard_signed; y: fp32
+ * row-major [batch][ldy].
+ * Requirements: k % 1024 == 0, 1 <= batch <= 8 (TQ_ERR_SHAPE); x, signs
+ * 16-byte aligned, ldx a multiple of 8 (TQ_ERR_ALIGN); ldx >= k, ldy >= n
+ * (TQ_ERR_ARG).  Covered: PQ2_0_G128 with batch 1 and k <= 11264; any other
+ * valid request returns TQ_ERR_UNSUPPORTED with nothing enqueued. */
+tq_status tq_rotated_gemv_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
+                                   int32_t format, int64_t n, int64_t k,
+                                   const void *x, int32_t x_dtype, int64_t batch,
+                                   int64_t ldx, const uint16_t *signs_bf16,
+                                   float *y, int64_t ldy, void *stream);
+
 /* Prefill GEMM: Y[m][n] = sum_g s[n][g] * sum_{j in g} t[n][j] * X[m][j]
  * for m < M rows of rotated activations X (x_dtype TQ_F16 or TQ_BF16,
  * row-major [M][ldx], 16-byte aligned, ldx a multiple of 8) against a

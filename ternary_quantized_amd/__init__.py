@@ -37,6 +37,7 @@ EXPORTS = (
     "tq_last_error", "tq_version", "tq_geometry_get", "tq_pack_rowsplit",
     "tq_unpack_rowsplit", "tq_hadamard_signed", "tq_gemv_rowsplit",
     "tq_gemm_rowsplit", "tq_embed_rows_inverse", "tq_decode_rowsplit",
+    "tq_rotated_gemv_rowsplit",
 )
 
 
@@ -73,6 +74,8 @@ def lib():
             "tq_hadamard_signed": [_vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp, _i32, _i64, _vp],
             "tq_gemv_rowsplit": [_vp, _u64, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _i64, _vp],
             "tq_gemm_rowsplit": [_vp, _u64, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _i32, _i64, _vp],
+            "tq_rotated_gemv_rowsplit": [_vp, _u64, _i32, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _vp,
+                                         _i64, _vp],
             "tq_embed_rows_inverse": [_vp, _u64, _i32, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp],
             "tq_decode_rowsplit": [_vp, _u64, _i32, _i64, _i64, _vp, _i64, _vp, _vp, _vp],
         }
@@ -196,6 +199,25 @@ def gemv_rowsplit(payload, fmt, n, k, xrot, out=None):
                                   _fmt(fmt), n, k, xrot.data_ptr(), _dtype_code(xrot), batch,
                                   xrot.stride(0), out.data_ptr(), out.stride(0),
                                   _stream(xrot.device)))
+    return out
+
+
+def rotated_gemv_rowsplit(payload, fmt, n, k, x, signs, out=None):
+    """y [batch, n] fp32 = decode-GEMV of the signed transform of x [batch, k]
+    (unrotated), in one launch."""
+    torch = _torch()
+    _dev(payload, "payload")
+    _dev(x, "x")
+    _dev(signs, "signs")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    batch = x.shape[0]
+    if out is None:
+        out = torch.empty((batch, n), dtype=torch.float32, device=x.device)
+    _check(lib().tq_rotated_gemv_rowsplit(payload.data_ptr(), payload.numel() * payload.element_size(),
+                                          _fmt(fmt), n, k, x.data_ptr(), _dtype_code(x), batch,
+                                          x.stride(0), signs.data_ptr(), out.data_ptr(),
+                                          out.stride(0), _stream(x.device)))
     return out
 
 

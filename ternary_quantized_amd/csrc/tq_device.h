@@ -7,6 +7,8 @@
 namespace tq {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 enum { FMT_PQ2 = 142, FMT_PTQ1 = 143 };
@@ -76,6 +78,45 @@ __device__ __forceinline__ void load16(const void *p, int64_t i, float v[16]) {
 }
 
 // Store 16 consecutive elements at element i (16-byte aligned).
+// load16 split in two: the raw 16-byte vectors of 16 elements (issue), and
+// their conversion to fp32 (use), so that other loads can be issued between.
+template <int DT>
+struct Raw16 {
+  u32x4 q[DT == DT_F32 ? 4 : 2];
+};
+
+template <int DT>
+__device__ __forceinline__ void load16_raw(const void *p, int64_t i, Raw16<DT> &r) {
+  const u32x4 *q = reinterpret_cast<const u32x4 *>(static_cast<const char *>(p) +
+                                                    i * (DT == DT_F32 ? 4 : 2));
+#pragma unroll
+  for (int j = 0; j < (DT == DT_F32 ? 4 : 2); ++j) r.q[j] = q[j];
+}
+
+template <int DT>
+__device__ __forceinline__ void convert16(const Raw16<DT> &r, float v[16]) {
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * j + e] = __uint_as_float(r.q[j][e]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t lo = (uint16_t)(r.q[j][e] & 0xFFFF), hi = (uint16_t)(r.q[j][e] >> 16);
+        if constexpr (DT == DT_BF16) {
+          v[8 * j + 2 * e] = bf16_to_f32(lo);
+          v[8 * j + 2 * e + 1] = bf16_to_f32(hi);
+        } else {
+          v[8 * j + 2 * e] = f16_to_f32(lo);
+          v[8 * j + 2 * e + 1] = f16_to_f32(hi);
+        }
+      }
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ void store16(void *p, int64_t i, const float v[16]) {
   if constexpr (DT == DT_F32) {

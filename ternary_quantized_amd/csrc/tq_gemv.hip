@@ -26,9 +26,6 @@
 
 namespace tq {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ half2_t cvt_codes(uint32_t v, int sel) {
   switch (sel) {
     case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 2.0f, 0);
@@ -212,14 +209,12 @@ __device__ __forceinline__ void load_raw(const Planes &p, const ChunkPtr<FMT, CW
 
 // Loader cursor: the plane pointers of one lane chunk at row `row`,
 // advanced by fixed byte strides (no 64-bit multiplies in the loop).  Rows
-// past n load from the last row instead (a valid address) and are masked.
+// past n are skipped (no memory access) and masked when reduced.
 template <int FMT, int CW>
 struct Cursor {
   const uint8_t *b, *h;
   const uint16_t *s;
   int64_t row;
-  const uint8_t *lb, *lh;  // last row
-  const uint16_t *ls;
   int64_t sb, sh, ss, srow;  // strides per step
 };
 
@@ -231,9 +226,6 @@ __device__ __forceinline__ Cursor<FMT, CW> make_cursor(const Planes &p, const Ch
   k.b = cp.base + row * p.base_row;
   k.h = cp.high + row * p.high_row;
   k.s = cp.scale + row * p.groups;
-  k.lb = cp.base + (p.n - 1) * p.base_row;
-  k.lh = cp.high + (p.n - 1) * p.high_row;
-  k.ls = cp.scale + (p.n - 1) * p.groups;
   k.sb = row_step * p.base_row;
   k.sh = row_step * p.high_row;
   k.ss = row_step * p.groups;
@@ -243,28 +235,32 @@ __device__ __forceinline__ Cursor<FMT, CW> make_cursor(const Planes &p, const Ch
 
 template <int FMT, int CW>
 __device__ __forceinline__ void load_next(Cursor<FMT, CW> &k, int64_t n, Raw<FMT, CW> &r) {
-  const bool in = k.row < n;
-  const uint8_t *b = in ? k.b : k.lb;
-  if constexpr (FMT == FMT_PQ2) {
-    if constexpr (CW >= 64) {
+  // rows past n are not read at all (masked lanes make no memory access):
+  // pointing them at one shared valid row would funnel every such request
+  // of the grid into one L2 channel
+  if (k.row < n) {
+    const uint8_t *b = k.b;
+    if constexpr (FMT == FMT_PQ2) {
+      if constexpr (CW >= 64) {
 #pragma unroll
-      for (int q = 0; q < CW / 64; ++q) {
-        u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(b) + q);
-        r.w[4 * q] = t[0]; r.w[4 * q + 1] = t[1]; r.w[4 * q + 2] = t[2]; r.w[4 * q + 3] = t[3];
+        for (int q = 0; q < CW / 64; ++q) {
+          u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(b) + q);
+          r.w[4 * q] = t[0]; r.w[4 * q + 1] = t[1]; r.w[4 * q + 2] = t[2]; r.w[4 * q + 3] = t[3];
+        }
+      } else if constexpr (CW == 32) {
+        u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(b));
+        r.w[0] = t[0]; r.w[1] = t[1];
+      } else {
+        r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(b));
       }
-    } else if constexpr (CW == 32) {
-      u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(b));
-      r.w[0] = t[0]; r.w[1] = t[1];
+      r.h = 0;
     } else {
       r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(b));
+      r.w[1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(b + 4));
+      r.h = *k.h;
     }
-    r.h = 0;
-  } else {
-    r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(b));
-    r.w[1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(b + 4));
-    r.h = *(in ? k.h : k.lh);
-  }
-  r.s = *(in ? k.s : k.ls);
+    r.s = *k.s;
+  }  // else: the slot keeps stale data; that row is masked when reduced
   k.b += k.sb;
   k.h += k.sh;
   k.s += k.ss;
@@ -446,9 +442,8 @@ __global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restri
     __syncthreads();
   }
 
-  // ---- weight ring: loads are branch-free (idle lanes read chunk 0, rows
-  // past n read the last row) and masked afterwards; pointers advance by
-  // fixed strides
+  // ---- weight ring: idle lanes read chunk 0 and are masked afterwards,
+  // rows past n are not read; pointers advance by fixed strides
   const ChunkPtr<FMT, CW> cp = chunk_ptr<FMT, CW>(p, cc);
   const int64_t row_step = G * teams;  // rows between consecutive passes
   Cursor<FMT, CW> cur = make_cursor<FMT, CW>(p, cp, (int64_t)blockIdx.x * teams + team, row_step);
@@ -508,8 +503,8 @@ __global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restri
 // (16 weights, inside group 32*A + 8*j + l/8).  Every load instruction of the
 // wave covers one contiguous span, the wave's partial sums are reduced with
 // DPP row shifts and four lane reads, and lane 0 writes the row: waves never
-// synchronise, so each is an independent persistent stream over rows
-// gw, gw + W, gw + 2W, ... (W = waves in the grid) with D rows in flight.
+// synchronise, so each is an independent persistent stream over blocks of D
+// consecutive rows (W = waves in the grid) with D rows in flight.
 template <int A, int BQ>
 struct WRaw {
   uint32_t w[4 * A + BQ];
@@ -524,15 +519,172 @@ __device__ __forceinline__ float wave_sum(float v) {
          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
-template <int A, int BQ, int D, int XD>
-__global__ __launch_bounds__(256) void gemv_wave_kernel(Planes p, const void *__restrict__ x,
-                                                        float *__restrict__ y) {
-  const int lane = threadIdx.x & 63;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t W = (int64_t)gridDim.x * 4;
-  constexpr int NP = A + BQ;  // pieces per lane
+// Sums of up to 8 rows' per-lane partials v[0..D-1] over the 64 lanes of a
+// wave, all at once: two swap stages halve the values per lane while pairing
+// lane halves (32) and 16-lane rows, a rotate by 8 inside each 16-lane row
+// merges the last two values, and three DPP row shifts finish each 8-lane
+// group.  Lane 8g+7 then holds the total of row bitrev3(g); it is returned
+// for that lane (other lanes return garbage) together with the row index.
+template <int D>
+__device__ __forceinline__ float rows8_sum(const float (&v)[D], int lane, int &row) {
+  static_assert(D >= 1 && D <= 8, "at most 8 rows");
+  auto bits = [](float f) { return __builtin_bit_cast(unsigned, f); };
+  auto flt = [](unsigned u) { return __builtin_bit_cast(float, u); };
+  float u[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) u[d] = d < D ? v[d] : 0.0f;
+  // lanes 0-31 | 32-63 of s1[i] carry rows 2i | 2i+1
+  float s1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto r = __builtin_amdgcn_permlane32_swap(bits(u[2 * i]), bits(u[2 * i + 1]), false, false);
+    s1[i] = flt(r[0]) + flt(r[1]);
+  }
+  // 16-lane rows R0..R3 of s2[i] carry rows 4i + (0, 2, 1, 3)
+  float s2[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const auto r = __builtin_amdgcn_permlane16_swap(bits(s1[2 * i]), bits(s1[2 * i + 1]), false, false);
+    s2[i] = flt(r[0]) + flt(r[1]);
+  }
+  // lanes 0-7 of each 16-lane row keep s2[0], lanes 8-15 s2[1]; each adds
+  // the matching value of the other half-row (row_ror:8)
+  const bool hi = (lane & 8) != 0;
+  const float keep = hi ? s2[1] : s2[0];
+  const float give = hi ? s2[0] : s2[1];
+  float x = keep + flt(__builtin_amdgcn_update_dpp(0u, bits(give), 0x128, 0xF, 0xF, false));
+  x += flt(__builtin_amdgcn_update_dpp(0u, bits(x), 0x111, 0xF, 0xF, true));
+  x += flt(__builtin_amdgcn_update_dpp(0u, bits(x), 0x112, 0xF, 0xF, true));
+  x += flt(__builtin_amdgcn_update_dpp(0u, bits(x), 0x114, 0xF, 0xF, true));
+  const int g = lane >> 3;
+  row = ((g & 1) << 2) | (g & 2) | ((g >> 2) & 1);
+  return x;
+}
 
-  // ---- activation pieces (binary16 pairs: weights (e, e+8) of each dword)
+// Workgroups are fat (WPG waves, one workgroup per CU) because the
+// activation row is read once per workgroup: every wave reading it on its own
+// sends thousands of requests to the same few L2 lines.  It is staged into
+// LDS as binary16 (rounded as the kernel rounds any input) and each wave then
+// takes its pieces from there.
+//
+// With FUSED set the kernel also performs the signed transform of its input
+// ([tensorsharp] §4.2: a projection input is rotated by H(D.x)/32 per
+// 1024-element block): x is then the unrotated activation row and the
+// workgroup transforms it into LDS (binary16, rounded exactly as the
+// standalone transform with binary16 output rounds it) while its first D
+// rows of weights are in flight, so one launch covers the whole step.
+template <int A, int BQ, int D, int XD, bool FUSED, int WPG>
+__global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const void *__restrict__ x,
+                                                             const uint16_t *__restrict__ signs,
+                                                             float *__restrict__ y) {
+  constexpr int NB = 4 * A + BQ;  // 1024-element blocks in a row
+  constexpr int NP = A + BQ;      // pieces per lane
+  __shared__ __attribute__((aligned(16))) uint16_t xl[NB * 1024];
+  const int lane = threadIdx.x & 63;
+  // the wave index is made explicitly uniform so that row offsets live in
+  // scalar registers and every load is (scalar row base + lane offset)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t gw = (int64_t)blockIdx.x * WPG + wave;
+  const int64_t W = (int64_t)gridDim.x * WPG;
+
+  // ---- rows: in pass q wave gw takes the D consecutive rows (q*W + gw)*D
+  // + d, so each wave streams one contiguous span of every plane; the launch
+  // picks D so that every wave has the same share.  Slot loads are
+  // unconditional: a branch around them would stop the compiler from
+  // counting the loads still in flight, and it would then wait for all of
+  // them at every row.  A slot whose next row lies past n re-reads the row
+  // it already holds (fb), so such loads stay spread over the planes.
+  const uint32_t o0 = 16 * lane, o1 = 1024 * A + 4 * lane;  // base bytes
+  const uint32_t q0 = lane / 2, q1 = 32 * A + lane / 8;     // scale entries
+  auto load_row = [&](int64_t row, int64_t fb, WRaw<A, BQ> &r) {
+    const int64_t rr = row < p.n ? row : fb;
+    const uint8_t *rb = p.base + rr * p.base_row;
+    const uint16_t *rs = p.scale + rr * p.groups;
+#pragma unroll
+    for (int i = 0; i < A; ++i) {
+      const u32x4 t =
+          __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(rb + (o0 + 1024 * i)));
+      r.w[4 * i] = t[0]; r.w[4 * i + 1] = t[1]; r.w[4 * i + 2] = t[2]; r.w[4 * i + 3] = t[3];
+      r.s[i] = rs[q0 + 32 * i];
+    }
+#pragma unroll
+    for (int j = 0; j < BQ; ++j) {
+      r.w[4 * A + j] =
+          __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(rb + (o1 + 256 * j)));
+      r.s[A + j] = rs[q1 + 8 * j];
+    }
+  };
+
+  // ---- 1. activation loads first, and waited for before any weight row is
+  // requested: issued alongside the rows they would queue in DRAM behind the
+  // whole weight stream of the chip.  Fused: wave w owns blocks
+  // w, w+WPG, ...; unfused: thread t converts 16-element chunks t,
+  // t+64*WPG, ...  Indexes past the end re-read the last block or chunk, so
+  // the loads stay unconditional.
+  constexpr int NI = FUSED ? (NB + WPG - 1) / WPG : (NB * 64 + 64 * WPG - 1) / (64 * WPG);
+  Raw16<XD> xraw[NI];
+  u32x4 sraw[FUSED ? NI : 1][2];
+  auto item = [&](int i) -> int64_t {  // first element of item i of this thread
+    if constexpr (FUSED) {
+      const int blk = wave + WPG * i < NB ? wave + WPG * i : NB - 1;
+      return (int64_t)blk * 1024 + 16 * lane;
+    } else {
+      const int c = (int)threadIdx.x + 64 * WPG * i;
+      return 16 * (int64_t)(c < NB * 64 ? c : NB * 64 - 1);
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    load16_raw<XD>(x, item(i), xraw[i]);
+    if constexpr (FUSED) {
+      const u32x4 *sp = reinterpret_cast<const u32x4 *>(signs + item(i));
+      sraw[i][0] = sp[0];
+      sraw[i][1] = sp[1];
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. activations into LDS as binary16
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const bool mine = FUSED ? wave + WPG * i < NB : (int)threadIdx.x + 64 * WPG * i < NB * 64;
+    if (mine) {
+      float v[16];
+      convert16<XD>(xraw[i], v);
+      if constexpr (FUSED) {
+        const uint32_t sw[8] = {sraw[i][0][0], sraw[i][0][1], sraw[i][0][2], sraw[i][0][3],
+                                sraw[i][1][0], sraw[i][1][1], sraw[i][1][2], sraw[i][1][3]};
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          v[e] = apply_sign(v[e], (uint16_t)(sw[e >> 1] >> (16 * (e & 1))));
+        wht1024_wave(v, lane);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] *= 0.03125f;
+      }
+      uint32_t h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        h[e] = (uint32_t)f32_to_f16(v[2 * e]) | ((uint32_t)f32_to_f16(v[2 * e + 1]) << 16);
+      u32x4 *dst = reinterpret_cast<u32x4 *>(xl + item(i));
+      dst[0] = (u32x4){h[0], h[1], h[2], h[3]};
+      dst[1] = (u32x4){h[4], h[5], h[6], h[7]};
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. the lane's pieces, as binary16 pairs (weights (e, e+8) of each
+  // dword) and their sums
+  auto load_act = [&](int64_t idx, float v[16]) {
+    const u32x4 *q = reinterpret_cast<const u32x4 *>(xl + idx);
+    const u32x4 a0 = q[0], a1 = q[1];
+    const uint32_t w[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = f16_to_f32((uint16_t)(w[i] & 0xFFFF));
+      v[2 * i + 1] = f16_to_f32((uint16_t)(w[i] >> 16));
+    }
+  };
   half2_t xp[4 * A + BQ][8];
   float xs[NP];
   {
@@ -540,10 +692,10 @@ __global__ __launch_bounds__(256) void gemv_wave_kernel(Planes p, const void *__
     for (int i = 0; i < A; ++i) {
       float v[64];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) load16<XD>(x, 4096 * i + 64 * lane + 16 * q, v + 16 * q);
+      for (int q = 0; q < 4; ++q) load_act(4096 * i + 64 * lane + 16 * q, v + 16 * q);
       float sum = 0.0f;
 #pragma unroll
-      for (int q = 0; q < 64; ++q) { v[q] = (float)(_Float16)v[q]; sum += v[q]; }
+      for (int q = 0; q < 64; ++q) sum += v[q];
       xs[i] = sum;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
@@ -553,10 +705,10 @@ __global__ __launch_bounds__(256) void gemv_wave_kernel(Planes p, const void *__
 #pragma unroll
     for (int j = 0; j < BQ; ++j) {
       float v[16];
-      load16<XD>(x, 4096 * A + 1024 * j + 16 * lane, v);
+      load_act(4096 * A + 1024 * j + 16 * lane, v);
       float sum = 0.0f;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) { v[q] = (float)(_Float16)v[q]; sum += v[q]; }
+      for (int q = 0; q < 16; ++q) sum += v[q];
       xs[A + j] = sum;
 #pragma unroll
       for (int e = 0; e < 8; ++e) xp[4 * A + j][e] = pack_h2(v[e], v[e + 8]);
@@ -564,47 +716,27 @@ __global__ __launch_bounds__(256) void gemv_wave_kernel(Planes p, const void *__
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- per-lane plane offsets inside a row
-  const uint8_t *b0 = p.base + 16 * lane;
-  const uint8_t *b1 = p.base + 1024 * A + 4 * lane;
-  const uint16_t *s0 = p.scale + lane / 2;
-  const uint16_t *s1 = p.scale + 32 * A + lane / 8;
-  auto load_row = [&](int64_t row, WRaw<A, BQ> &r) {
-    const int64_t rr = row < p.n ? row : p.n - 1;
-    const uint8_t *rb0 = b0 + rr * p.base_row;
-    const uint8_t *rb1 = b1 + rr * p.base_row;
-    const uint16_t *rs0 = s0 + rr * p.groups;
-    const uint16_t *rs1 = s1 + rr * p.groups;
-#pragma unroll
-    for (int i = 0; i < A; ++i) {
-      const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(rb0 + 1024 * i));
-      r.w[4 * i] = t[0]; r.w[4 * i + 1] = t[1]; r.w[4 * i + 2] = t[2]; r.w[4 * i + 3] = t[3];
-      r.s[i] = rs0[32 * i];
-    }
-#pragma unroll
-    for (int j = 0; j < BQ; ++j) {
-      r.w[4 * A + j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(rb1 + 256 * j));
-      r.s[A + j] = rs1[8 * j];
-    }
-  };
-
+  // ---- 4. the first D weight rows, only now: once a CU's memory queue fills
+  // with row loads, a wave stalls at its next load issue until rows arrive,
+  // and the short set-up above would wait for the weight stream
   WRaw<A, BQ> ring[D];
+  const int64_t first = gw * D < p.n ? gw * D : p.n - 1;
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    load_row(gw + d * W, ring[d]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  for (int64_t base = gw; base < p.n; base += D * W) {
+  for (int d = 0; d < D; ++d) load_row(gw * D + d, first, ring[d]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  for (int64_t base = gw * D; base < p.n; base += (int64_t)D * W) {
+    float part[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      const int64_t row = base + d * W;
-      // sum over the lane's pieces of s * (sum code*x - sum x)
+      // sum over the lane's pieces of s * (sum code*x - sum x); the first
+      // product of each class starts from 0 instead of a zeroed register
       float acc = 0.0f;
 #pragma unroll
       for (int pc = 0; pc < NP; ++pc) {
         const int nd = pc < A ? 4 : 1;
         const int d0 = pc < A ? 4 * pc : 4 * A + (pc - A);
-        float a[5] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        float a[5];
 #pragma unroll
         for (int q = 0; q < nd; ++q) {
           const uint32_t w = ring[d].w[d0 + q], w10 = w >> 10;
@@ -612,41 +744,87 @@ __global__ __launch_bounds__(256) void gemv_wave_kernel(Planes p, const void *__
                                  w & 0x00C000C0u, w & 0x03000300u, w10 & 0x00030003u,
                                  w10 & 0x000C000Cu, w10 & 0x00300030u};
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            a[e < 5 ? e : e - 5] = dot2(bits_h2(t[e]), xp[d0 + q][e], a[e < 5 ? e : e - 5]);
+          for (int e = 0; e < 8; ++e) {
+            const int c = e < 5 ? e : e - 5;
+            const bool first_term = q == 0 && e < 5;
+            a[c] = __builtin_amdgcn_fdot2(bits_h2(t[e]), xp[d0 + q][e], first_term ? 0.0f : a[c],
+                                          false);
+          }
         }
         const float cx = a[0] * 16777216.0f + a[1] * 4194304.0f + a[2] * 1048576.0f +
                          a[3] * 262144.0f + a[4] * 65536.0f;
         acc += f16_to_f32((uint16_t)ring[d].s[pc]) * (cx - xs[pc]);
       }
-      // refill the slot with the row D steps ahead
-      load_row(row + D * W, ring[d]);
-      const float tot = wave_sum(acc);
-      if (lane == 0 && row < p.n) y[row] = tot;
+      part[d] = acc;
+      // refill the slot with its row of the next pass
+      load_row(base + d + (int64_t)D * W, base + d < p.n ? base + d : p.n - 1, ring[d]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    int r;
+    const float tot = rows8_sum<D>(part, lane, r);
+    if ((lane & 7) == 7 && r < D && base + r < p.n) y[base + r] = tot;
   }
 }
 
-template <int A, int BQ, int XD>
-static hipError_t gemv_wave_go(const Planes &p, const void *x, float *y, hipStream_t st) {
-  constexpr int D = 8;
-  auto kern = gemv_wave_kernel<A, BQ, D, XD>;
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-  const int64_t blocks_needed = (p.n + 3) / 4;
-  const int64_t slots = (int64_t)device_cus() * per_cu;
-  const int64_t grid = blocks_needed < slots ? blocks_needed : slots;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, st, p, x, y);
+template <int A, int BQ, int D, int XD, bool FUSED, int WPG>
+static hipError_t gemv_wave_launch(const Planes &p, const void *x, const uint16_t *signs, float *y,
+                                   int64_t waves, hipStream_t st) {
+  const int64_t grid = (waves + WPG - 1) / WPG;
+  hipLaunchKernelGGL((gemv_wave_kernel<A, BQ, D, XD, FUSED, WPG>), dim3((unsigned)grid),
+                     dim3(64 * WPG), 0, st, p, x, signs, y);
   return hipGetLastError();
 }
 
-template <int A, int BQ>
-static hipError_t gemv_wave_dt(const Planes &p, const void *x, int xd, float *y, hipStream_t st) {
-  if (xd == DT_F32) return gemv_wave_go<A, BQ, DT_F32>(p, x, y, st);
-  if (xd == DT_BF16) return gemv_wave_go<A, BQ, DT_BF16>(p, x, y, st);
-  return gemv_wave_go<A, BQ, DT_F16>(p, x, y, st);
+// Row split: for each ring depth D in {4, 6, 8} (D rows per wave and pass)
+// take as many workgroups per CU as fit, the fewest passes that cover n, and
+// then the fewest waves; keep the D whose busiest CU has the fewest rows
+// (ties: the deeper ring).  Rows past n in a wave's last block re-read the
+// row their slot already holds.  Workgroup size by register need: three
+// waves per SIMD up to k = 5120 (WPG 12), two up to k = 7168 (WPG 8), one
+// beyond (WPG 4).
+template <int A, int BQ, int XD, bool FUSED>
+static hipError_t gemv_wave_go(const Planes &p, const void *x, const uint16_t *signs, float *y,
+                               hipStream_t st) {
+  constexpr int NBK = 4 * A + BQ;
+  constexpr int WPG = NBK <= 5 ? 12 : NBK <= 7 ? 8 : 4;
+  const int cus = device_cus();
+  const void *kerns[3] = {
+      reinterpret_cast<const void *>(gemv_wave_kernel<A, BQ, 4, XD, FUSED, WPG>),
+      reinterpret_cast<const void *>(gemv_wave_kernel<A, BQ, 6, XD, FUSED, WPG>),
+      reinterpret_cast<const void *>(gemv_wave_kernel<A, BQ, 8, XD, FUSED, WPG>)};
+  const int depth[3] = {4, 6, 8};
+  int best = -1;
+  int64_t best_rows = 0, best_waves = 0;
+  for (int i = 0; i < 3; ++i) {
+    if (i == 2 && NBK == 5) continue;  // ring 8 at k = 5120 needs one register too many
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kerns[i], 64 * WPG, 0) != hipSuccess ||
+        per_cu < 1)
+      continue;  // this depth does not fit a workgroup on a CU
+    const int64_t D = depth[i];
+    const int64_t slots = (int64_t)WPG * cus * per_cu;
+    const int64_t passes = (p.n + slots * D - 1) / (slots * D);
+    const int64_t waves = (p.n + D * passes - 1) / (D * passes);
+    const int64_t wgs = (waves + WPG - 1) / WPG;
+    const int64_t rows_cu = ((wgs + cus - 1) / cus) * WPG * D * passes;
+    if (best < 0 || rows_cu <= best_rows) {
+      best = i;
+      best_rows = rows_cu;
+      best_waves = waves;
+    }
+  }
+  if (best < 0) return hipErrorInvalidConfiguration;
+  if (best == 0) return gemv_wave_launch<A, BQ, 4, XD, FUSED, WPG>(p, x, signs, y, best_waves, st);
+  if (best == 1) return gemv_wave_launch<A, BQ, 6, XD, FUSED, WPG>(p, x, signs, y, best_waves, st);
+  return gemv_wave_launch<A, BQ, 8, XD, FUSED, WPG>(p, x, signs, y, best_waves, st);
+}
+
+template <int A, int BQ, bool FUSED>
+static hipError_t gemv_wave_dt(const Planes &p, const void *x, int xd, const uint16_t *signs,
+                               float *y, hipStream_t st) {
+  if (xd == DT_F32) return gemv_wave_go<A, BQ, DT_F32, FUSED>(p, x, signs, y, st);
+  if (xd == DT_BF16) return gemv_wave_go<A, BQ, DT_BF16, FUSED>(p, x, signs, y, st);
+  return gemv_wave_go<A, BQ, DT_F16, FUSED>(p, x, signs, y, st);
 }
 
 // k = 1024*m with m <= 11: pieces A = m/4 kilobytes + BQ = m%4 blocks.
@@ -654,19 +832,21 @@ static bool gemv_wave_fits(const Planes &p) {
   return p.fmt == FMT_PQ2 && p.k % 1024 == 0 && p.k / 1024 >= 1 && p.k / 1024 <= 11;
 }
 
-static hipError_t gemv_wave(const Planes &p, const void *x, int xd, float *y, hipStream_t st) {
+template <bool FUSED>
+static hipError_t gemv_wave(const Planes &p, const void *x, int xd, const uint16_t *signs, float *y,
+                            hipStream_t st) {
   switch (p.k / 1024) {
-    case 1: return gemv_wave_dt<0, 1>(p, x, xd, y, st);
-    case 2: return gemv_wave_dt<0, 2>(p, x, xd, y, st);
-    case 3: return gemv_wave_dt<0, 3>(p, x, xd, y, st);
-    case 4: return gemv_wave_dt<1, 0>(p, x, xd, y, st);
-    case 5: return gemv_wave_dt<1, 1>(p, x, xd, y, st);
-    case 6: return gemv_wave_dt<1, 2>(p, x, xd, y, st);
-    case 7: return gemv_wave_dt<1, 3>(p, x, xd, y, st);
-    case 8: return gemv_wave_dt<2, 0>(p, x, xd, y, st);
-    case 9: return gemv_wave_dt<2, 1>(p, x, xd, y, st);
-    case 10: return gemv_wave_dt<2, 2>(p, x, xd, y, st);
-    default: return gemv_wave_dt<2, 3>(p, x, xd, y, st);
+    case 1: return gemv_wave_dt<0, 1, FUSED>(p, x, xd, signs, y, st);
+    case 2: return gemv_wave_dt<0, 2, FUSED>(p, x, xd, signs, y, st);
+    case 3: return gemv_wave_dt<0, 3, FUSED>(p, x, xd, signs, y, st);
+    case 4: return gemv_wave_dt<1, 0, FUSED>(p, x, xd, signs, y, st);
+    case 5: return gemv_wave_dt<1, 1, FUSED>(p, x, xd, signs, y, st);
+    case 6: return gemv_wave_dt<1, 2, FUSED>(p, x, xd, signs, y, st);
+    case 7: return gemv_wave_dt<1, 3, FUSED>(p, x, xd, signs, y, st);
+    case 8: return gemv_wave_dt<2, 0, FUSED>(p, x, xd, signs, y, st);
+    case 9: return gemv_wave_dt<2, 1, FUSED>(p, x, xd, signs, y, st);
+    case 10: return gemv_wave_dt<2, 2, FUSED>(p, x, xd, signs, y, st);
+    default: return gemv_wave_dt<2, 3, FUSED>(p, x, xd, signs, y, st);
   }
 }
 
@@ -985,7 +1165,7 @@ hipError_t launch_gemv(const Planes &p, const void *x, int xd, int64_t batch, in
   const bool wide32 = p.k / 32 > 1024, wide16 = p.k / 16 > 1024;
   if (gemv_mfma_fits(p) && batch >= 2 && batch <= 4)
     return gemv_mfma<true>(p, x, xd, batch, ldx, y, ldy, st);
-  if (batch <= 1 && gemv_wave_fits(p)) return gemv_wave(p, x, xd, y, st);
+  if (batch <= 1 && gemv_wave_fits(p)) return gemv_wave<false>(p, x, xd, nullptr, y, st);
   if (batch <= 1 || (wide32 && batch <= 2)) {
     if (batch <= 1) return gemv_b1<FMT_PQ2, 64>(p, x, xd, ldx, y, ldy, st);
     return gemv_go<FMT_PQ2, 64, 2, 2>(p, x, xd, batch, ldx, y, ldy, st);
@@ -998,6 +1178,15 @@ hipError_t launch_gemv(const Planes &p, const void *x, int xd, int64_t batch, in
   if (batch <= 4) return gemv_go<FMT_PQ2, 32, 4, 2>(p, x, xd, batch, ldx, y, ldy, st);
   if (wide16) return gemv_go<FMT_PQ2, 32, 8, 1>(p, x, xd, batch, ldx, y, ldy, st);
   return gemv_go<FMT_PQ2, 16, 8, 2>(p, x, xd, batch, ldx, y, ldy, st);
+}
+
+bool rotated_gemv_fused(const Planes &p, int64_t batch) {
+  return batch == 1 && gemv_wave_fits(p);
+}
+
+hipError_t launch_rotated_gemv(const Planes &p, const void *x, int xd, const uint16_t *signs,
+                               float *y, hipStream_t st) {
+  return gemv_wave<true>(p, x, xd, signs, y, st);
 }
 
 }  // namespace tq

@@ -293,6 +293,36 @@ tq_status tq_gemv_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
                        "tq_gemv_rowsplit");
 }
 
+tq_status tq_rotated_gemv_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
+                                   int32_t format, int64_t n, int64_t k, const void *x,
+                                   int32_t x_dtype, int64_t batch, int64_t ldx,
+                                   const uint16_t *signs_bf16, float *y, int64_t ldy,
+                                   void *stream) {
+  tq_geometry g;
+  tq::Planes p;
+  tq_status st = check_device_payload(payload, payload_bytes, format, n, k, &g, &p);
+  if (st != TQ_OK) return st;
+  if (k % 1024)
+    return fail(TQ_ERR_SHAPE, "k=%lld: the transform needs a multiple of the 1024-element block",
+                (long long)k);
+  if (batch < 1 || batch > 8) return fail(TQ_ERR_SHAPE, "batch=%lld must be in 1..8", (long long)batch);
+  if (!dtype_ok(x_dtype)) return fail(TQ_ERR_ARG, "x_dtype must be TQ_F32, TQ_BF16 or TQ_F16");
+  if (!x || !y) return fail(TQ_ERR_ARG, "x and y must be non-NULL");
+  st = check_signs(signs_bf16);
+  if (st != TQ_OK) return st;
+  if (ldx < k || ldy < n) return fail(TQ_ERR_ARG, "ldx must be >= k and ldy >= n");
+  if (!aligned(x, 16) || ldx % 8)
+    return fail(TQ_ERR_ALIGN, "x must be 16-byte aligned with ldx a multiple of 8");
+  if (!aligned(y, 4)) return fail(TQ_ERR_ALIGN, "y must be 4-byte aligned");
+  if (!tq::rotated_gemv_fused(p, batch))
+    return fail(TQ_ERR_UNSUPPORTED,
+                "the fused transform + GEMV covers PQ2_0_G128, batch 1, k <= 11264; "
+                "use tq_hadamard_signed then tq_gemv_rowsplit");
+  return device_status(tq::launch_rotated_gemv(p, x, x_dtype, signs_bf16, y,
+                                               (hipStream_t)stream),
+                       "tq_rotated_gemv_rowsplit");
+}
+
 tq_status tq_gemm_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
                            int32_t format, int64_t n, int64_t k, const void *x,
                            int32_t x_dtype, int64_t m, int64_t ldx, void *y,

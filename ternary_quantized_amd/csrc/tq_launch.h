@@ -34,6 +34,12 @@ hipError_t launch_gemm(const Planes &p, const uint16_t *x, int x_dtype,
 
 int64_t gemv_max_k(int fmt);
 
+// Signed transform fused into the GEMV (one launch): supported shapes, and
+// the launch itself (x unrotated, signs bf16 +-1).
+bool rotated_gemv_fused(const Planes &p, int64_t batch);
+hipError_t launch_rotated_gemv(const Planes &p, const void *x, int x_dtype,
+                               const uint16_t *signs, float *y, hipStream_t st);
+
 // compute units of the current device (cached per device)
 int device_cus();
 

@@ -136,6 +136,18 @@ def test_device_entry_validation_without_gpu():
     assert L.tq_gemm_rowsplit(DEV, pb, 142, 64, 1024, DEV, 0, 4, 1024, DEV, 0, 64, None) == 1
     assert L.tq_gemm_rowsplit(DEV, pb, 142, 64, 1024, DEV, 2, 4, 1024, DEV, 2, 64, None) == 1
     assert L.tq_gemm_rowsplit(DEV, pb, 143, 64, 1024, DEV, 2, 4, 1024, DEV, 0, 64, None) == 3
+    # fused transform + GEMV: k multiple of 1024, null signs, then the
+    # requests the one-launch kernel does not cover (PTQ1_0, batch > 1)
+    f = L.tq_rotated_gemv_rowsplit
+    pb4 = tq.geometry("PQ2_0_G128", 64, 1152)["payload_bytes"]
+    assert f(DEV, pb4, 142, 64, 1152, DEV, 0, 1, 1152, DEV, DEV, 64, None) == 5
+    assert f(DEV, pb, 142, 64, 1024, DEV, 0, 1, 1024, None, DEV, 64, None) == 1
+    assert f(DEV, pb, 142, 64, 1024, DEV, 0, 9, 1024, DEV, DEV, 64, None) == 5
+    assert f(DEV, pb, 142, 64, 1024, DEV + 8, 0, 1, 1024, DEV, DEV, 64, None) == 4
+    assert f(DEV, pb, 142, 64, 1024, DEV, 0, 2, 1024, DEV, DEV, 64, None) == 6
+    pt = tq.geometry("PTQ1_0_G128", 64, 1024)["payload_bytes"]
+    assert f(DEV, pt, 143, 64, 1024, DEV, 0, 1, 1024, DEV, DEV, 64, None) == 6
+    assert b"tq_hadamard_signed then tq_gemv_rowsplit" in L.tq_last_error()
     # embedding: k must be a multiple of 1024
     pb3 = tq.geometry("PQ2_0_G128", 64, 1152)["payload_bytes"]
     assert L.tq_embed_rows_inverse(DEV, pb3, 142, 64, 1152, DEV, 4, DEV, DEV, 1152, None, None) == 5

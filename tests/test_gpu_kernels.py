@@ -129,6 +129,51 @@ def test_gemv_parity(fmt, n, k, batch):
     assert_within(to_f64(torch, y), expect, bound, "gemv")
 
 
+# ------------------------------------------- fused transform + GEMV ---
+@pytest.mark.parametrize("n,k", [(1, 1024), (77, 3072), (1000, 5120), (300, 11264)])
+@pytest.mark.parametrize("xdt", ["f32", "bf16", "f16"])
+def test_rotated_gemv_parity_and_equals_two_launches(n, k, xdt):
+    """One launch = tq_hadamard_signed (binary16 out) then tq_gemv_rowsplit,
+    bit for bit; and within the oracle's bound of W . H(D.x)/32 computed in
+    float64 from the unrotated input."""
+    rng = np.random.default_rng(n + k)
+    trits = synth.trits_sparse(rng, n, k)
+    sb = synth.scale_bits_lognormal(rng, n, synth.groups_of(k))
+    payload = tq.pack_rowsplit("PQ2_0_G128", trits, sb)
+    x = rand_x(rng, 1, k, xdt, scale=3.0)
+    sign_bits = synth.sign_bits(rng, k)
+    say("rotated gemv n=%d k=%d x=%s" % (n, k, xdt))
+    pd, xd, sd = dev(torch, payload), x_dev(torch, x, xdt), signs_dev(torch, sign_bits)
+    y = tq.rotated_gemv_rowsplit(pd, "PQ2_0_G128", n, k, xd, sd)
+    xr = tq.hadamard_signed(xd, sd, out_dtype=torch.float16)
+    y2 = tq.gemv_rowsplit(pd, "PQ2_0_G128", n, k, xr)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    xrot = T.forward(x_f64(x, xdt), T.bf16_bits_to_f64(sign_bits))
+    expect, bound = P.project_payload("PQ2_0_G128", n, k, payload, xrot)
+    # x' is rounded to binary16 (relative 2^-11 per element) before the dot
+    w_abs_x = (bound - P.ABS) / P.REL
+    assert_within(to_f64(torch, y), expect, bound + 2.0 ** -11 * w_abs_x, "rotated gemv")
+
+
+def test_rotated_gemv_unsupported_requests_enqueue_nothing():
+    rng = np.random.default_rng(9)
+    n, k = 64, 2048
+    sign_bits = synth.sign_bits(rng, k)
+    sd = signs_dev(torch, sign_bits)
+    x = x_dev(torch, rand_x(rng, 2, k, "f16"), "f16")
+    for fmt, batch in (("PTQ1_0_G128", 1), ("PQ2_0_G128", 2)):
+        trits = synth.trits_sparse(rng, n, k)
+        sb = synth.scale_bits_lognormal(rng, n, synth.groups_of(k))
+        pd = dev(torch, tq.pack_rowsplit(fmt, trits, sb))
+        out = torch.full((batch, n), 7.0, device="cuda")
+        with pytest.raises(tq.TQError) as e:
+            tq.rotated_gemv_rowsplit(pd, fmt, n, k, x[:batch], sd, out=out)
+        assert e.value.status == 6
+        torch.cuda.synchronize()
+        assert bool((out == 7.0).all())
+
+
 @pytest.mark.parametrize("fmt", ["PQ2_0_G128", "PTQ1_0_G128"])
 def test_gemv_integer_exact_and_deterministic(fmt):
     # scales 1.0 and integer activations in [-8, 8] (exact in binary16):

@@ -41,6 +41,11 @@ def test_config_gemv_full(cfg):
     y2 = tq.gemv_rowsplit(pd, c["fmt"], c["n"], c["k"], xr)
     torch.cuda.synchronize()
     assert torch.equal(y, y2)
+    # the one-launch decode step gives the same bits as the two launches
+    xd = x_dev(torch, x, c["x_dtype"])
+    yf = tq.rotated_gemv_rowsplit(pd, c["fmt"], c["n"], c["k"], xd, signs_dev(torch, c["sign_bits"]))
+    torch.cuda.synchronize()
+    assert torch.equal(yf, y)
     xr64 = T.forward(x_f64(x, c["x_dtype"]), T.bf16_bits_to_f64(c["sign_bits"]))
     expect, bound = P.project_payload(c["fmt"], c["n"], c["k"], payload, xr64)
     assert_within(to_f64(torch, y), expect, bound, "config %d" % cfg)
