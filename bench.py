@@ -51,17 +51,19 @@ def copies_for(nbytes, minimum=2):
 
 
 def event_timed(torch, fn, launches):
-    """Mean duration (s) of fn(i) over `launches` calls, each bracketed by HIP
-    events on the current stream."""
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(launches)]
+    """Mean duration (s) of fn(i) over `launches` back-to-back calls: one HIP
+    event before the first and one after the last, both on the current
+    stream (per-call event pairs would add their own cost to every call)."""
+    fn(0)
+    torch.cuda.current_stream().synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
     for i in range(launches):
-        starts[i].record()
         fn(i)
-        ends[i].record()
-    torch.cuda.synchronize()
-    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return float(np.mean(ms)) / 1e3, float(np.median(ms)) / 1e3
+    end.record()
+    end.synchronize()
+    return start.elapsed_time(end) / 1e3 / launches
 
 
 def load_counters(name, source):
@@ -163,12 +165,12 @@ def main():
     # ------------------------------ roofline of the fused decode kernel
     with torch.cuda.stream(stream):
         launches = 8 * ncopy
-        step_mean, step_median = event_timed(torch, step, launches)
+        step_mean = event_timed(torch, step, launches)
         # the same step as two launches (transform, then GEMV), for context
         tq.hadamard_signed(x, signs, out=xrot)
-        gemv_mean, _ = event_timed(
+        gemv_mean = event_timed(
             torch, lambda i: tq.gemv_rowsplit(copies[i % ncopy], fmt, n, k, xrot, out=y), launches)
-        wht_mean, _ = event_timed(torch, lambda i: tq.hadamard_signed(x, signs, out=xrot), 64)
+        wht_mean = event_timed(torch, lambda i: tq.hadamard_signed(x, signs, out=xrot), 64)
         g2 = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g2, stream=stream):
             for i in range(args.steps):
@@ -188,7 +190,7 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "gemv_wave_kernel<A=1, BQ=1, ring 6, x bf16, fused transform>",
                 "bytes_per_launch": step_bytes, "mean_launch_us": round(step_mean * 1e6, 3),
-                "median_launch_us": round(step_median * 1e6, 3), "launches": launches}
+                "launches": launches, "timing": "hip events around back-to-back launches"}
     del copies
     torch.cuda.empty_cache()
 
@@ -256,7 +258,7 @@ def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream):
         for b in (1, 4, 8):
             xr = tq.hadamard_signed(x3[:b], s3, out_dtype=torch.float16)
             yb = torch.empty((b, n3), dtype=torch.float32, device=xr.device)
-            mean, _ = event_timed(torch, lambda i: tq.gemv_rowsplit(cps[i % nc], c3["fmt"], n3, k3,
+            mean = event_timed(torch, lambda i: tq.gemv_rowsplit(cps[i % nc], c3["fmt"], n3, k3,
                                                                   xr, out=yb), 4 * nc)
             byts = p3.size + 2 * b * k3 + 4 * b * n3
             res["cfg3_ptq1_down_b%d" % b] = {"mean_launch_us": round(mean * 1e6, 3),
@@ -276,7 +278,7 @@ def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream):
         s4 = bits_dev(c4["sign_bits"], torch.bfloat16)
         xr = tq.hadamard_signed(x4, s4, out_dtype=torch.float16)
         y4 = torch.empty((1, n4), dtype=torch.float32, device=xr.device)
-        mean, _ = event_timed(torch, lambda i: tq.gemv_rowsplit(cps[i % 2], c4["fmt"], n4, k4, xr,
+        mean = event_timed(torch, lambda i: tq.gemv_rowsplit(cps[i % 2], c4["fmt"], n4, k4, xr,
                                                               out=y4), 20)
         byts = p4.size + 2 * k4 + 4 * n4
         res["cfg4_head_b1"] = {"mean_launch_us": round(mean * 1e6, 3),
@@ -284,7 +286,7 @@ def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream):
                                "frac_hbm": round(byts / mean / 1e9 / HBM_PEAK_GBS, 4)}
         ids = to_dev(c4["ids"])
         emb = torch.empty((64, k4), dtype=torch.float32, device=xr.device)
-        mean, _ = event_timed(torch, lambda i: tq.embed_rows_inverse(cps[i % 2], c4["fmt"], n4, k4,
+        mean = event_timed(torch, lambda i: tq.embed_rows_inverse(cps[i % 2], c4["fmt"], n4, k4,
                                                                    ids, s4, out=emb), 20)
         res["cfg4_embed_64_rows_us"] = round(mean * 1e6, 3)
         del cps
@@ -297,9 +299,9 @@ def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream):
         x5 = bits_dev(c5["x"], torch.bfloat16)
         s5 = bits_dev(c5["sign_bits"], torch.bfloat16)
         xr5 = torch.empty((x5.shape[0], k5), dtype=torch.float16, device=x5.device)
-        wmean, _ = event_timed(torch, lambda i: tq.hadamard_signed(x5, s5, out=xr5), 10)
+        wmean = event_timed(torch, lambda i: tq.hadamard_signed(x5, s5, out=xr5), 10)
         y5 = torch.empty((x5.shape[0], n5), dtype=torch.float32, device=x5.device)
-        gmean, gmed = event_timed(torch, lambda i: tq.gemm_rowsplit(p5, c5["fmt"], n5, k5, xr5,
+        gmean = event_timed(torch, lambda i: tq.gemm_rowsplit(p5, c5["fmt"], n5, k5, xr5,
                                                                   out=y5), 10)
         flops = 2.0 * x5.shape[0] * n5 * k5
         res["cfg5_prefill_gemm"] = {"m": int(x5.shape[0]), "n": n5, "k": k5,
