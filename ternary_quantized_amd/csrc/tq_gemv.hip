@@ -118,15 +118,12 @@ __device__ __forceinline__ float convert_x_chunk(const XRaw<FMT, CW, XD> &r, int
       for (int e = 0; e < 8; ++e) xp[8 * d + e] = pack_h2(v[16 * d + e], v[16 * d + e + 8]);
     }
   } else {
+    // byte pair pp covers trits 10pp..10pp+4 (first byte) and 10pp+5..10pp+9
+    // (second); digit i of both bytes forms pair 5pp+i
 #pragma unroll
-    for (int pp = 0; pp < 3; ++pp) {
-      const int b0 = 10 * pp, b1 = 10 * pp + 5;  // first trit of the byte pair
-      xp[5 * pp + 0] = pack_h2(v[b0 + 0], v[b0 + 1]);
-      xp[5 * pp + 1] = pack_h2(v[b0 + 2], v[b0 + 3]);
-      xp[5 * pp + 2] = pack_h2(v[b1 + 0], v[b1 + 1]);
-      xp[5 * pp + 3] = pack_h2(v[b1 + 2], v[b1 + 3]);
-      xp[5 * pp + 4] = pack_h2(v[b0 + 4], v[b1 + 4]);
-    }
+    for (int pp = 0; pp < 3; ++pp)
+#pragma unroll
+      for (int i = 0; i < 5; ++i) xp[5 * pp + i] = pack_h2(v[10 * pp + i], v[10 * pp + 5 + i]);
     xp[15] = pack_h2(v[30], v[31]);
   }
   float s = 0.0f;
@@ -306,28 +303,34 @@ __device__ __forceinline__ void chunk_dot(const Raw<FMT, CW> &r, int64_t c,
     // the lane's 6 base bytes start 0 or 2 bytes into the loaded window
     const uint64_t win = ((uint64_t)r.w[1] << 32) | r.w[0];
     const uint64_t bytes = (q & 1) ? (win >> 16) : win;
-    const uint32_t *lut_even = lut, *lut_odd = lut + 256, *lut_high = lut + 512;
+    // lut[v]: the five radix-3 digits of byte v as 2-bit codes, digit i at
+    // bits 2i.  Two bytes side by side (second one shifted up 16) give, for
+    // each digit i, a binary16 pair whose zero-exponent fields are the codes
+    // times 4^i * 2^-24: the same subnormal-class products as PQ2_0, one
+    // mask and one dot2 per two trits.
+    float a[B][5];
 #pragma unroll
     for (int pp = 0; pp < 3; ++pp) {
-      const uint32_t e0 = lut_even[(bytes >> (16 * pp)) & 0xFF];
-      const uint32_t e1 = lut_odd[(bytes >> (16 * pp + 8)) & 0xFF];
-      const uint32_t e4 = e0 | e1;
-      const half2_t w0 = cvt_codes(e0, 0), w1 = cvt_codes(e0, 1);
-      const half2_t w2 = cvt_codes(e1, 0), w3 = cvt_codes(e1, 1);
-      const half2_t w4 = cvt_codes(e4, 2);
+      const uint32_t dw = lut[(bytes >> (16 * pp)) & 0xFF] |
+                          (lut[(bytes >> (16 * pp + 8)) & 0xFF] << 16);
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        part[b] = dot2(w0, xp[b][5 * pp + 0], part[b]);
-        part[b] = dot2(w1, xp[b][5 * pp + 1], part[b]);
-        part[b] = dot2(w2, xp[b][5 * pp + 2], part[b]);
-        part[b] = dot2(w3, xp[b][5 * pp + 3], part[b]);
-        part[b] = dot2(w4, xp[b][5 * pp + 4], part[b]);
+      for (int i = 0; i < 5; ++i) {
+        const half2_t t = bits_h2(dw & (0x00030003u << (2 * i)));
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+          a[b][i] = __builtin_amdgcn_fdot2(t, xp[b][5 * pp + i], pp == 0 ? 0.0f : a[b][i], false);
       }
     }
-    const uint32_t eh = lut_high[r.h & 0xFF];
-    const half2_t wh = (q & 1) ? cvt_codes(eh, 1) : cvt_codes(eh, 0);
+    // the chunk's two high trits: digits 2(q&1) and 2(q&1)+1 of its high
+    // byte, placed as a class-0 pair
+    const uint32_t wh = lut[r.h & 0xFF] >> (4 * (q & 1));
+    const half2_t th = bits_h2((wh & 3u) | ((wh & 0xCu) << 14));
 #pragma unroll
-    for (int b = 0; b < B; ++b) part[b] = dot2(wh, xp[b][15], part[b]);
+    for (int b = 0; b < B; ++b) {
+      a[b][0] = dot2(th, xp[b][15], a[b][0]);
+      part[b] = a[b][0] * 16777216.0f + a[b][1] * 4194304.0f + a[b][2] * 1048576.0f +
+                a[b][3] * 262144.0f + a[b][4] * 65536.0f;
+    }
   }
 }
 
@@ -376,7 +379,7 @@ __global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restri
                                                   int64_t batch, int64_t ldx,
                                                   float *__restrict__ y, int64_t ldy,
                                                   int chunks, int cseg, int teams) {
-  __shared__ uint32_t lut[FMT == FMT_PTQ1 ? 768 : 1];
+  __shared__ uint32_t lut[FMT == FMT_PTQ1 ? 256 : 1];
   __shared__ float red[D * B * (1024 / SEG)];  // [slot][b][segment]
   // activation pairs of every chunk in decode order, plus chunk sums:
   // staged once per workgroup (teams share chunks)
@@ -390,17 +393,12 @@ __global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restri
   const int64_t G = gridDim.x;
 
   if constexpr (FMT == FMT_PTQ1) {
-    // Tables mapping a byte v to its radix-3 digits as fp4 nibbles:
-    //  even/odd: digits 0..3 in nibbles 0..3, digit 4 in nibble 4 (even) or
-    //  nibble 5 (odd), so OR-ing an even and an odd entry pairs the two
-    //  fifth digits in byte 2; high: digits 0..3 in nibbles 0..3.
+    // byte v -> its radix-3 digits floor(v / 3^i) mod 3, i < 5, as 2-bit
+    // codes at bits 2i (high bytes use digits 0..3 of the same table)
     for (int v = t; v < 256; v += blockDim.x) {
-      uint32_t d[5], u = (uint32_t)v;
-      for (int i = 0; i < 5; ++i) { d[i] = u % 3u; u /= 3u; }
-      const uint32_t low = d[0] | (d[1] << 4) | (d[2] << 8) | (d[3] << 12);
-      lut[v] = low | (d[4] << 16);
-      lut[256 + v] = low | (d[4] << 20);
-      lut[512 + v] = low;
+      uint32_t u = (uint32_t)v, w = 0;
+      for (int i = 0; i < 5; ++i) { w |= (u % 3u) << (2 * i); u /= 3u; }
+      lut[v] = w;
     }
   }
   // ---- stage the activations, one batch row at a time: thread i converts
@@ -1159,7 +1157,16 @@ hipError_t launch_gemv(const Planes &p, const void *x, int xd, int64_t batch, in
     if (batch <= 1) return gemv_b1<FMT_PTQ1, 32>(p, x, xd, ldx, y, ldy, st);
     if (batch <= 2) return gemv_go<FMT_PTQ1, 32, 2, 4>(p, x, xd, batch, ldx, y, ldy, st);
     if (batch <= 4) return gemv_go<FMT_PTQ1, 32, 4, 2>(p, x, xd, batch, ldx, y, ldy, st);
-    return gemv_go<FMT_PTQ1, 32, 8, 1>(p, x, xd, batch, ldx, y, ldy, st);
+    // 5..8 rows: one pass while a row's team fits a 512-lane workgroup; wider
+    // rows would need a 1024-lane workgroup, whose 128-register lanes cannot
+    // hold 8 rows of activation pairs, so they run as two passes of <= 4 rows
+    if ((p.k / 32 + 15) / 16 * 16 <= 512)
+      return gemv_go<FMT_PTQ1, 32, 8, 1>(p, x, xd, batch, ldx, y, ldy, st);
+    hipError_t e = gemv_go<FMT_PTQ1, 32, 4, 2>(p, x, xd, 4, ldx, y, ldy, st);
+    if (e != hipSuccess) return e;
+    const int64_t esz = xd == DT_F32 ? 4 : 2;
+    return gemv_go<FMT_PTQ1, 32, 4, 2>(p, static_cast<const char *>(x) + 4 * ldx * esz, xd,
+                                       batch - 4, ldx, y + 4 * ldy, ldy, st);
   }
   // a chunk never spans two groups (64 | 128); wide rows need wider chunks
   const bool wide32 = p.k / 32 > 1024, wide16 = p.k / 16 > 1024;
