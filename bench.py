@@ -51,18 +51,27 @@ def copies_for(nbytes, minimum=2):
 
 
 def event_timed(torch, fn, launches):
-    """Mean duration (s) of fn(i) over `launches` back-to-back calls: one HIP
-    event before the first and one after the last, both on the current
-    stream (per-call event pairs would add their own cost to every call)."""
+    """Mean GPU duration (s) of fn(i) over `launches` calls.  The calls are
+    captured once as a HIP graph on the current stream and the replay is
+    bracketed by two HIP events on that stream: a host loop of launches
+    cannot keep up with kernels of a few microseconds, so it would time the
+    host, not the kernel."""
+    stream = torch.cuda.current_stream()
     fn(0)
-    torch.cuda.current_stream().synchronize()
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(launches):
+            fn(i)
+    g.replay()
+    stream.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(launches):
-        fn(i)
-    end.record()
+    start.record(stream)
+    g.replay()
+    end.record(stream)
     end.synchronize()
+    del g
     return start.elapsed_time(end) / 1e3 / launches
 
 
@@ -190,7 +199,7 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "gemv_wave_kernel<A=1, BQ=1, ring 6, x bf16, fused transform>",
                 "bytes_per_launch": step_bytes, "mean_launch_us": round(step_mean * 1e6, 3),
-                "launches": launches, "timing": "hip events around back-to-back launches"}
+                "launches": launches, "timing": "hip events around a graph replay of back-to-back launches"}
     del copies
     torch.cuda.empty_cache()
 

@@ -151,30 +151,80 @@ __device__ __forceinline__ float apply_sign(float v, uint16_t s) {
   return __uint_as_float(__float_as_uint(v) ^ ((uint32_t)(s & 0x8000u) << 16));
 }
 
-// In-wave Walsh-Hadamard butterfly of one 1024-element block held as 16
-// consecutive elements per lane (element 16*lane + i in v[i]).  Computes the
-// unnormalised Sylvester transform in natural order: stages on index bits
-// 0..3 run inside the lane, bits 4..9 pair lanes lane ^ 1 .. lane ^ 32.
-__device__ __forceinline__ void wht1024_wave(float v[16], int lane) {
+// In-wave Walsh-Hadamard butterfly of one 1024-element block (unnormalised
+// Sylvester transform, natural order).  On entry lane l holds elements
+// 16l + i in v[i]; on return v[i] holds element wht_out_index(l, i) =
+// (i & 3) + 4l + 256(i >> 2).  All butterflies run inside registers, in the
+// order of the index bits 0, 1, ..., 9 (each a + b for the lower element and
+// a - b for the upper one), with two transposes through the wave's private
+// scratch `sc` (1024 floats in LDS) in between:
+//   bits 0-3: v[i] = element 16l + i
+//   bits 4-7: after the first transpose, v[i] = element (l & 15) + 16i + 256(l >> 4)
+//   bits 8-9: after the second, v[i] = element (i & 3) + 4l + 256(i >> 2)
+// A wave's LDS operations complete in order, so no barrier is needed.
+__device__ __forceinline__ int wht_out_index(int lane, int i) {
+  return (i & 3) + 4 * lane + 256 * (i >> 2);
+}
+
+template <int HFIRST, int HLAST>
+__device__ __forceinline__ void wht_regs(float v[16]) {
 #pragma unroll
-  for (int h = 1; h < 16; h <<= 1) {
+  for (int h = HFIRST; h <= HLAST; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if ((i & h) == 0) {
-        float a = v[i], b = v[i + h];
+        const float a = v[i], b = v[i + h];
         v[i] = a + b;
         v[i + h] = a - b;
       }
     }
   }
+}
+
+__device__ __forceinline__ void wht1024_wave(float v[16], int lane, float *sc) {
+  wht_regs<1, 8>(v);
+  {
+    u32x4 *w = reinterpret_cast<u32x4 *>(sc + 16 * lane);
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const bool upper = (lane & m) != 0;
+    for (int j = 0; j < 4; ++j)
+      w[j] = (u32x4){__float_as_uint(v[4 * j]), __float_as_uint(v[4 * j + 1]),
+                     __float_as_uint(v[4 * j + 2]), __float_as_uint(v[4 * j + 3])};
+  }
+  const int t1 = (lane & 15) + 256 * (lane >> 4);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float p = __shfl_xor(v[i], m, 64);
-      v[i] = upper ? (p - v[i]) : (v[i] + p);
+  for (int i = 0; i < 16; ++i) v[i] = sc[t1 + 16 * i];
+  wht_regs<1, 8>(v);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sc[t1 + 16 * i] = v[i];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const u32x4 r = *reinterpret_cast<const u32x4 *>(sc + 4 * lane + 256 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[4 * g + j] = __uint_as_float(r[j]);
+  }
+  wht_regs<4, 8>(v);
+}
+
+// 4 consecutive elements (as fp32) to/from memory of type DT.
+template <int DT>
+__device__ __forceinline__ void store4(void *p, int64_t i, const float v[4]) {
+  if constexpr (DT == DT_F32) {
+    *reinterpret_cast<float4 *>(static_cast<float *>(p) + i) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    uint32_t w[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      uint32_t lo, hi;
+      if constexpr (DT == DT_BF16) {
+        lo = f32_to_bf16(v[2 * e]);
+        hi = f32_to_bf16(v[2 * e + 1]);
+      } else {
+        lo = f32_to_f16(v[2 * e]);
+        hi = f32_to_f16(v[2 * e + 1]);
+      }
+      w[e] = lo | (hi << 16);
     }
+    *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(p) + i) = (u32x2){w[0], w[1]};
   }
 }
 

@@ -578,6 +578,8 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   constexpr int NB = 4 * A + BQ;  // 1024-element blocks in a row
   constexpr int NP = A + BQ;      // pieces per lane
   __shared__ __attribute__((aligned(16))) uint16_t xl[NB * 1024];
+  // the transform's per-wave scratch (waves below NB own blocks)
+  __shared__ __attribute__((aligned(16))) float wsc[FUSED ? (NB < WPG ? NB : WPG) : 1][1024];
   const int lane = threadIdx.x & 63;
   // the wave index is made explicitly uniform so that row offsets live in
   // scalar registers and every load is (scalar row base + lane offset)
@@ -656,17 +658,27 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
 #pragma unroll
         for (int e = 0; e < 16; ++e)
           v[e] = apply_sign(v[e], (uint16_t)(sw[e >> 1] >> (16 * (e & 1))));
-        wht1024_wave(v, lane);
+        // v[4g + j] leaves the transform holding element 256g + 4*lane + j
+        // of the block
+        wht1024_wave(v, lane, wsc[wave]);
+        uint32_t h[8];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) v[e] *= 0.03125f;
+        for (int e = 0; e < 8; ++e)
+          h[e] = (uint32_t)f32_to_f16(v[2 * e] * 0.03125f) |
+                 ((uint32_t)f32_to_f16(v[2 * e + 1] * 0.03125f) << 16);
+        const int64_t blk = (int64_t)(wave + WPG * i) * 1024;
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<u32x2 *>(xl + blk + 256 * g + 4 * lane) = (u32x2){h[2 * g], h[2 * g + 1]};
+      } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          h[e] = (uint32_t)f32_to_f16(v[2 * e]) | ((uint32_t)f32_to_f16(v[2 * e + 1]) << 16);
+        u32x4 *dst = reinterpret_cast<u32x4 *>(xl + item(i));
+        dst[0] = (u32x4){h[0], h[1], h[2], h[3]};
+        dst[1] = (u32x4){h[4], h[5], h[6], h[7]};
       }
-      uint32_t h[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        h[e] = (uint32_t)f32_to_f16(v[2 * e]) | ((uint32_t)f32_to_f16(v[2 * e + 1]) << 16);
-      u32x4 *dst = reinterpret_cast<u32x4 *>(xl + item(i));
-      dst[0] = (u32x4){h[0], h[1], h[2], h[3]};
-      dst[1] = (u32x4){h[4], h[5], h[6], h[7]};
     }
   }
   __syncthreads();

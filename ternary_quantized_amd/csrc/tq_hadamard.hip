@@ -6,11 +6,12 @@
 // Walsh-Hadamard transform.  [tensorsharp] §4.4: the embedding row is looked
 // up, dequantised and inverse-transformed.
 //
-// One wave transforms one 1024-element block: each lane holds 16 consecutive
+// One wave transforms one 1024-element block: each lane loads 16 consecutive
 // elements (one 64-byte fp32 / 32-byte 16-bit vector load per lane, so a
-// wave reads the block as one contiguous span), the four low index bits are
-// butterflied in registers and the six high bits across lanes.  The 1/32
-// normalisation and the sign flips are exact.
+// wave reads the block as one contiguous span); every butterfly runs in
+// registers, with two transposes through the wave's own LDS scratch (see
+// wht1024_wave), and each lane writes its results as four runs of four
+// consecutive elements.  The 1/32 normalisation and the sign flips are exact.
 
 #include "tq_device.h"
 #include "tq_launch.h"
@@ -21,36 +22,41 @@ template <int XD, int YD>
 __global__ __launch_bounds__(256) void hadamard_kernel(
     const void *x, int64_t ldx, int64_t rows, int64_t nblocks,
     const uint16_t *__restrict__ signs, int inverse, void *y, int64_t ldy) {
+  __shared__ __attribute__((aligned(16))) float scratch[4][1024];
   const int lane = threadIdx.x & 63;
-  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wave;
   if (item >= rows * nblocks) return;
   const int64_t row = item / nblocks;
-  const int64_t col = (item % nblocks) * 1024 + 16 * lane;
+  const int64_t blk = (item % nblocks) * 1024;
+  const int64_t col = blk + 16 * lane;
 
   float v[16];
   load16<XD>(x, row * ldx + col, v);
-  uint16_t s[16];
-  {
+  if (!inverse) {
     const uint4 *sp = reinterpret_cast<const uint4 *>(signs + col);
     uint4 a = sp[0], b = sp[1];
     uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      s[2 * j] = (uint16_t)(w[j] & 0xFFFF);
-      s[2 * j + 1] = (uint16_t)(w[j] >> 16);
+    for (int i = 0; i < 16; ++i) v[i] = apply_sign(v[i], (uint16_t)(w[i >> 1] >> (16 * (i & 1))));
+  }
+  wht1024_wave(v, lane, scratch[wave]);
+  // v[4g + j] now holds element blk + 256g + 4*lane + j
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int64_t c = blk + 256 * g + 4 * lane;
+    float o[4];
+    if (inverse) {
+      const u32x2 sw = *reinterpret_cast<const u32x2 *>(signs + c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        o[j] = apply_sign(v[4 * g + j] * 0.03125f, (uint16_t)(sw[j >> 1] >> (16 * (j & 1))));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = v[4 * g + j] * 0.03125f;
     }
+    store4<YD>(y, row * ldy + c, o);
   }
-  if (!inverse) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = apply_sign(v[i], s[i]);
-  }
-  wht1024_wave(v, lane);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    v[i] *= 0.03125f;
-    if (inverse) v[i] = apply_sign(v[i], s[i]);
-  }
-  store16<YD>(y, row * ldy + col, v);
 }
 
 template <int XD>
@@ -123,12 +129,14 @@ __global__ __launch_bounds__(256) void embed_kernel(Planes p, const int32_t *__r
                                                     const uint16_t *__restrict__ signs,
                                                     float *__restrict__ out, int64_t ldo,
                                                     int32_t *err_word) {
+  __shared__ __attribute__((aligned(16))) float scratch[4][1024];
   const int lane = threadIdx.x & 63;
   const int64_t nblocks = p.k / 1024;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= count * nblocks) return;
   const int64_t i = item / nblocks;
-  const int64_t col = (item % nblocks) * 1024 + 16 * lane;
+  const int64_t blk = (item % nblocks) * 1024;
+  const int64_t col = blk + 16 * lane;
   const int32_t id = ids[i];
   float v[16];
   if (id < 0 || (int64_t)id >= p.n) {
@@ -139,11 +147,18 @@ __global__ __launch_bounds__(256) void embed_kernel(Planes p, const int32_t *__r
     return;
   }
   decode16<FMT>(p, id, col, v);
-  wht1024_wave(v, lane);
-  const uint16_t *sp = signs + col;
+  wht1024_wave(v, lane, scratch[threadIdx.x >> 6]);
+  // v[4g + j] now holds element blk + 256g + 4*lane + j
 #pragma unroll
-  for (int e = 0; e < 16; ++e) v[e] = apply_sign(v[e] * 0.03125f, sp[e]);
-  store16<DT_F32>(out, i * ldo + col, v);
+  for (int g = 0; g < 4; ++g) {
+    const int64_t c = blk + 256 * g + 4 * lane;
+    const u32x2 sw = *reinterpret_cast<const u32x2 *>(signs + c);
+    float o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = apply_sign(v[4 * g + j] * 0.03125f, (uint16_t)(sw[j >> 1] >> (16 * (j & 1))));
+    store4<DT_F32>(out, i * ldo + c, o);
+  }
 }
 
 hipError_t launch_embed(const Planes &p, const int32_t *ids, int64_t count,
