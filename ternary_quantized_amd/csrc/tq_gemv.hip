@@ -41,6 +41,28 @@ __device__ __forceinline__ float dot2(half2_t a, half2_t b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
+// The first products of the five code classes, a[c] = t[c].lo*x[c].lo +
+// t[c].hi*x[c].hi, each from a zero accumulator.  They are taken in the
+// three-operand form: the compiler only emits the two-operand form, whose
+// accumulator is tied to the destination and would need five registers
+// cleared first.  A dot product's result may be read by a different vector
+// instruction only three wait states later, which the compiler cannot see
+// through the asm, so the block ends with those wait states itself.
+__device__ __forceinline__ void dot2_first5(const uint32_t (&t)[8], const half2_t *x, float (&a)[5]) {
+  asm("v_dot2_f32_f16 %0, %5, %10, 0\n\t"
+      "v_dot2_f32_f16 %1, %6, %11, 0\n\t"
+      "v_dot2_f32_f16 %2, %7, %12, 0\n\t"
+      "v_dot2_f32_f16 %3, %8, %13, 0\n\t"
+      "v_dot2_f32_f16 %4, %9, %14, 0\n\t"
+      "s_nop 2"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4])
+      : "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]), "v"(t[4]),
+        "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]));
+}
+
+// cache policy of a streaming (read-once) buffer load
+constexpr int CPOL_NT = 2;
+
 __device__ __forceinline__ half2_t pack_h2(float a, float b) {
   half2_t r;
   r.x = (_Float16)a;
@@ -594,23 +616,28 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   // counting the loads still in flight, and it would then wait for all of
   // them at every row.  A slot whose next row lies past n re-reads the row
   // it already holds (fb), so such loads stay spread over the planes.
-  const uint32_t o0 = 16 * lane, o1 = 1024 * A + 4 * lane;  // base bytes
-  const uint32_t q0 = lane / 2, q1 = 32 * A + lane / 8;     // scale entries
-  auto load_row = [&](int64_t row, int64_t fb, WRaw<A, BQ> &r) {
-    const int64_t rr = row < p.n ? row : fb;
-    const uint8_t *rb = p.base + rr * p.base_row;
-    const uint16_t *rs = p.scale + rr * p.groups;
+  // Row numbers are 32-bit (the launch guarantees n < 2^30): the scalar
+  // unit has no 64-bit ordered compare, so 64-bit row tests would run on the
+  // vector unit every row.
+  const int n32 = (int)p.n;
+  const int q0 = lane / 2, q1 = 32 * A + lane / 8;  // scale entries
+  auto load_row = [&](int row, int fb, WRaw<A, BQ> &r) {
+    const int rr = row < n32 ? row : fb;
+    // the row's base bytes as a buffer: the row address stays in scalar
+    // registers and each load adds only the lane's offset (a streaming load
+    // through a flat pointer would rebuild the 64-bit address every row)
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(p.base + (int64_t)rr * p.base_row), 0, (int)p.base_row, 0x00020000);
+    const uint16_t *rs = p.scale + (int64_t)rr * p.groups;
 #pragma unroll
     for (int i = 0; i < A; ++i) {
-      const u32x4 t =
-          __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(rb + (o0 + 1024 * i)));
+      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane + 1024 * i, 0, CPOL_NT);
       r.w[4 * i] = t[0]; r.w[4 * i + 1] = t[1]; r.w[4 * i + 2] = t[2]; r.w[4 * i + 3] = t[3];
       r.s[i] = rs[q0 + 32 * i];
     }
 #pragma unroll
     for (int j = 0; j < BQ; ++j) {
-      r.w[4 * A + j] =
-          __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(rb + (o1 + 256 * j)));
+      r.w[4 * A + j] = __builtin_amdgcn_raw_buffer_load_b32(rb, 1024 * A + 4 * lane + 256 * j, 0, CPOL_NT);
       r.s[A + j] = rs[q1 + 8 * j];
     }
   };
@@ -730,12 +757,13 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   // with row loads, a wave stalls at its next load issue until rows arrive,
   // and the short set-up above would wait for the weight stream
   WRaw<A, BQ> ring[D];
-  const int64_t first = gw * D < p.n ? gw * D : p.n - 1;
+  const int gw32 = (int)gw, W32 = (int)W;
+  const int first = gw32 * D < n32 ? gw32 * D : n32 - 1;
 #pragma unroll
-  for (int d = 0; d < D; ++d) load_row(gw * D + d, first, ring[d]);
+  for (int d = 0; d < D; ++d) load_row(gw32 * D + d, first, ring[d]);
   __builtin_amdgcn_sched_barrier(0);
 
-  for (int64_t base = gw * D; base < p.n; base += (int64_t)D * W) {
+  for (int base = gw32 * D; base < n32; base += D * W32) {
     float part[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -753,12 +781,11 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
           const uint32_t t[8] = {w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u,
                                  w & 0x00C000C0u, w & 0x03000300u, w10 & 0x00030003u,
                                  w10 & 0x000C000Cu, w10 & 0x00300030u};
+          if (q == 0) dot2_first5(t, xp[d0], a);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
+          for (int e = q == 0 ? 5 : 0; e < 8; ++e) {
             const int c = e < 5 ? e : e - 5;
-            const bool first_term = q == 0 && e < 5;
-            a[c] = __builtin_amdgcn_fdot2(bits_h2(t[e]), xp[d0 + q][e], first_term ? 0.0f : a[c],
-                                          false);
+            a[c] = __builtin_amdgcn_fdot2(bits_h2(t[e]), xp[d0 + q][e], a[c], false);
           }
         }
         const float cx = a[0] * 16777216.0f + a[1] * 4194304.0f + a[2] * 1048576.0f +
@@ -767,7 +794,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
       }
       part[d] = acc;
       // refill the slot with its row of the next pass
-      load_row(base + d + (int64_t)D * W, base + d < p.n ? base + d : p.n - 1, ring[d]);
+      load_row(base + d + D * W32, base + d < n32 ? base + d : n32 - 1, ring[d]);
       __builtin_amdgcn_sched_barrier(0);
     }
     int r;
@@ -806,7 +833,6 @@ static hipError_t gemv_wave_go(const Planes &p, const void *x, const uint16_t *s
   int best = -1;
   int64_t best_rows = 0, best_waves = 0;
   for (int i = 0; i < 3; ++i) {
-    if (i == 2 && NBK == 5) continue;  // ring 8 at k = 5120 needs one register too many
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kerns[i], 64 * WPG, 0) != hipSuccess ||
         per_cu < 1)
@@ -839,7 +865,8 @@ static hipError_t gemv_wave_dt(const Planes &p, const void *x, int xd, const uin
 
 // k = 1024*m with m <= 11: pieces A = m/4 kilobytes + BQ = m%4 blocks.
 static bool gemv_wave_fits(const Planes &p) {
-  return p.fmt == FMT_PQ2 && p.k % 1024 == 0 && p.k / 1024 >= 1 && p.k / 1024 <= 11;
+  return p.fmt == FMT_PQ2 && p.k % 1024 == 0 && p.k / 1024 >= 1 && p.k / 1024 <= 11 &&
+         p.n < (int64_t(1) << 30);
 }
 
 template <bool FUSED>
