@@ -24,6 +24,8 @@
 #include "tq_device.h"
 #include "tq_launch.h"
 
+#include <type_traits>
+
 namespace tq {
 
 __device__ __forceinline__ half2_t cvt_codes(uint32_t v, int sel) {
@@ -583,24 +585,35 @@ __device__ __forceinline__ float rows8_sum(const float (&v)[D], int lane, int &r
 
 // Workgroups are fat (WPG waves, one workgroup per CU) because the
 // activation row is read once per workgroup: every wave reading it on its own
-// sends thousands of requests to the same few L2 lines.  It is staged into
-// LDS as binary16 (rounded as the kernel rounds any input) and each wave then
-// takes its pieces from there.
+// sends thousands of requests to the same few L2 lines.  The first NB waves
+// ("staging" waves) stage it into LDS as binary16 pairs in the order the
+// decoder consumes them, lane-major so that every lane later reads its own
+// pairs with conflict-free 16-byte LDS reads, together with the sum of every
+// lane piece.  The other waves request their first D weight rows at once,
+// so the weight stream starts at the beginning of the kernel; the staging
+// waves request theirs after the staging barrier (a wave whose loads fill
+// the compute unit's memory queue stalls at its next load until rows
+// arrive, which would hold up the staging).
 //
 // With FUSED set the kernel also performs the signed transform of its input
 // ([tensorsharp] §4.2: a projection input is rotated by H(D.x)/32 per
-// 1024-element block): x is then the unrotated activation row and the
-// workgroup transforms it into LDS (binary16, rounded exactly as the
-// standalone transform with binary16 output rounds it) while its first D
-// rows of weights are in flight, so one launch covers the whole step.
+// 1024-element block): x is then the unrotated activation row, each staging
+// wave transforms its 1024-element blocks in registers and rounds them to
+// binary16 exactly as the standalone transform with binary16 output does,
+// so one launch covers the whole step with the same result as two.
 template <int A, int BQ, int D, int XD, bool FUSED, int WPG>
 __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const void *__restrict__ x,
                                                              const uint16_t *__restrict__ signs,
                                                              float *__restrict__ y) {
-  constexpr int NB = 4 * A + BQ;  // 1024-element blocks in a row
+  constexpr int NB = 4 * A + BQ;  // 1024-element blocks in a row = 16-weight dwords per lane
   constexpr int NP = A + BQ;      // pieces per lane
-  __shared__ __attribute__((aligned(16))) uint16_t xl[NB * 1024];
-  // the transform's per-wave scratch (waves below NB own blocks)
+  // Activation pairs: dword s of lane l (16 weights, pairs (e, e+8)) is held
+  // by quads (2s)*64 + l (pairs 0-3) and (2s+1)*64 + l (pairs 4-7).  Dword s
+  // of lane l is natural 16-element chunk 256i + 4l + d for s = 4i + d < 4A
+  // (a kilobyte piece) and 256A + 64j + l for s = 4A + j (a 256-byte piece).
+  __shared__ __attribute__((aligned(16))) u32x4 xq[NB * 128];
+  __shared__ float xsum[NP * 64];  // [piece][lane]: sum of the piece's binary16 activations
+  // the transform's per-wave scratch (staging waves only)
   __shared__ __attribute__((aligned(16))) float wsc[FUSED ? (NB < WPG ? NB : WPG) : 1][1024];
   const int lane = threadIdx.x & 63;
   // the wave index is made explicitly uniform so that row offsets live in
@@ -608,6 +621,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t gw = (int64_t)blockIdx.x * WPG + wave;
   const int64_t W = (int64_t)gridDim.x * WPG;
+  const bool stager = wave < NB;
 
   // ---- rows: in pass q wave gw takes the D consecutive rows (q*W + gw)*D
   // + d, so each wave streams one contiguous span of every plane; the launch
@@ -615,7 +629,8 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   // unconditional: a branch around them would stop the compiler from
   // counting the loads still in flight, and it would then wait for all of
   // them at every row.  A slot whose next row lies past n re-reads the row
-  // it already holds (fb), so such loads stay spread over the planes.
+  // it already holds (fb), so such loads stay spread over the planes; the
+  // last pass requests nothing (a wave cannot end before its loads return).
   // Row numbers are 32-bit (the launch guarantees n < 2^30): the scalar
   // unit has no 64-bit ordered compare, so 64-bit row tests would run on the
   // vector unit every row.
@@ -641,129 +656,141 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
       r.s[A + j] = rs[q1 + 8 * j];
     }
   };
-
-  // ---- 1. activation loads first, and waited for before any weight row is
-  // requested: issued alongside the rows they would queue in DRAM behind the
-  // whole weight stream of the chip.  Fused: wave w owns blocks
-  // w, w+WPG, ...; unfused: thread t converts 16-element chunks t,
-  // t+64*WPG, ...  Indexes past the end re-read the last block or chunk, so
-  // the loads stay unconditional.
-  constexpr int NI = FUSED ? (NB + WPG - 1) / WPG : (NB * 64 + 64 * WPG - 1) / (64 * WPG);
-  Raw16<XD> xraw[NI];
-  u32x4 sraw[FUSED ? NI : 1][2];
-  auto item = [&](int i) -> int64_t {  // first element of item i of this thread
-    if constexpr (FUSED) {
-      const int blk = wave + WPG * i < NB ? wave + WPG * i : NB - 1;
-      return (int64_t)blk * 1024 + 16 * lane;
-    } else {
-      const int c = (int)threadIdx.x + 64 * WPG * i;
-      return 16 * (int64_t)(c < NB * 64 ? c : NB * 64 - 1);
-    }
-  };
+  WRaw<A, BQ> ring[D];
+  const int gw32 = (int)gw, W32 = (int)W;
+  const int first = gw32 * D < n32 ? gw32 * D : n32 - 1;
+  auto load_first = [&]() {
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    load16_raw<XD>(x, item(i), xraw[i]);
-    if constexpr (FUSED) {
-      const u32x4 *sp = reinterpret_cast<const u32x4 *>(signs + item(i));
-      sraw[i][0] = sp[0];
-      sraw[i][1] = sp[1];
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    for (int d = 0; d < D; ++d) load_row(gw32 * D + d, first, ring[d]);
+  };
+
+  // ---- 1. non-staging waves: first D rows now
+  if (!stager) load_first();
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 2. activations into LDS as binary16
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const bool mine = FUSED ? wave + WPG * i < NB : (int)threadIdx.x + 64 * WPG * i < NB * 64;
-    if (mine) {
-      float v[16];
-      convert16<XD>(xraw[i], v);
+  // ---- 2. staging waves: activations -> binary16 pairs in LDS.  Fused:
+  // wave w transforms blocks w, w + WPG, ... (chunks 64*block + lane);
+  // unfused: thread t converts chunks t, t + 64*WPG, ...  Items past the end
+  // re-read the last block or chunk, so the loads stay unconditional.
+  if (stager) {
+    constexpr int NI = FUSED ? (NB + WPG - 1) / WPG : (NB * 64 + 64 * WPG - 1) / (64 * WPG);
+    Raw16<XD> xraw[NI];
+    u32x4 sraw[FUSED ? NI : 1][2];
+    auto item = [&](int i) -> int64_t {  // first element of item i of this thread
       if constexpr (FUSED) {
+        const int blk = wave + WPG * i < NB ? wave + WPG * i : NB - 1;
+        return (int64_t)blk * 1024 + 16 * lane;
+      } else {
+        const int c = (int)threadIdx.x + 64 * WPG * i;
+        return 16 * (int64_t)(c < NB * 64 ? c : NB * 64 - 1);
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      load16_raw<XD>(x, item(i), xraw[i]);
+      if constexpr (FUSED) {
+        const u32x4 *sp = reinterpret_cast<const u32x4 *>(signs + item(i));
+        sraw[i][0] = sp[0];
+        sraw[i][1] = sp[1];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const bool mine = FUSED ? wave + WPG * i < NB : (int)threadIdx.x + 64 * WPG * i < NB * 64;
+      if (!mine) continue;
+      // h[m]: binary16 elements 2m, 2m+1 of this thread's 16-element chunk
+      uint32_t h[8];
+      if constexpr (FUSED) {
+        float v[16];
+        convert16<XD>(xraw[i], v);
         const uint32_t sw[8] = {sraw[i][0][0], sraw[i][0][1], sraw[i][0][2], sraw[i][0][3],
                                 sraw[i][1][0], sraw[i][1][1], sraw[i][1][2], sraw[i][1][3]};
 #pragma unroll
         for (int e = 0; e < 16; ++e)
           v[e] = apply_sign(v[e], (uint16_t)(sw[e >> 1] >> (16 * (e & 1))));
         // v[4g + j] leaves the transform holding element 256g + 4*lane + j
-        // of the block
-        wht1024_wave(v, lane, wsc[wave]);
-        uint32_t h[8];
+        // of the block; the block goes back through the wave's scratch in
+        // natural order, and the lane takes chunk `lane` of it
+        float *sc = wsc[wave];
+        wht1024_wave(v, lane, sc);
+        uint16_t *nat = reinterpret_cast<uint16_t *>(sc);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          h[e] = (uint32_t)f32_to_f16(v[2 * e] * 0.03125f) |
-                 ((uint32_t)f32_to_f16(v[2 * e + 1] * 0.03125f) << 16);
-        const int64_t blk = (int64_t)(wave + WPG * i) * 1024;
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t lo = (uint32_t)f32_to_f16(v[4 * g] * 0.03125f) |
+                              ((uint32_t)f32_to_f16(v[4 * g + 1] * 0.03125f) << 16);
+          const uint32_t hi = (uint32_t)f32_to_f16(v[4 * g + 2] * 0.03125f) |
+                              ((uint32_t)f32_to_f16(v[4 * g + 3] * 0.03125f) << 16);
+          *reinterpret_cast<u32x2 *>(nat + 256 * g + 4 * lane) = (u32x2){lo, hi};
+        }
+        const u32x4 *q = reinterpret_cast<const u32x4 *>(nat + 16 * lane);
+        const u32x4 a0 = q[0], a1 = q[1];
+        h[0] = a0[0]; h[1] = a0[1]; h[2] = a0[2]; h[3] = a0[3];
+        h[4] = a1[0]; h[5] = a1[1]; h[6] = a1[2]; h[7] = a1[3];
+      } else if constexpr (XD == DT_F16) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *reinterpret_cast<u32x2 *>(xl + blk + 256 * g + 4 * lane) = (u32x2){h[2 * g], h[2 * g + 1]};
+        for (int m = 0; m < 4; ++m) { h[m] = xraw[i].q[0][m]; h[4 + m] = xraw[i].q[1][m]; }
       } else {
-        uint32_t h[8];
+        float v[16];
+        convert16<XD>(xraw[i], v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          h[e] = (uint32_t)f32_to_f16(v[2 * e]) | ((uint32_t)f32_to_f16(v[2 * e + 1]) << 16);
-        u32x4 *dst = reinterpret_cast<u32x4 *>(xl + item(i));
-        dst[0] = (u32x4){h[0], h[1], h[2], h[3]};
-        dst[1] = (u32x4){h[4], h[5], h[6], h[7]};
+        for (int m = 0; m < 8; ++m)
+          h[m] = (uint32_t)f32_to_f16(v[2 * m]) | ((uint32_t)f32_to_f16(v[2 * m + 1]) << 16);
+      }
+      // pairs (e, e+8) of the chunk and their sum
+      uint32_t pr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        pr[e] = __builtin_amdgcn_perm(h[4 + e / 2], h[e / 2], (e & 1) ? 0x07060302u : 0x05040100u);
+      float sum = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        sum = __builtin_amdgcn_fdot2(bits_h2(pr[e]), bits_h2(0x3C003C00u), sum, false);
+      const int c = FUSED ? (wave + WPG * i) * 64 + lane : (int)threadIdx.x + 64 * WPG * i;
+      int s, l;
+      if (c < 256 * A) {
+        s = 4 * (c >> 8) + (c & 3);
+        l = (c & 255) >> 2;
+      } else {
+        s = 4 * A + ((c - 256 * A) >> 6);
+        l = (c - 256 * A) & 63;
+      }
+      xq[(2 * s) * 64 + l] = (u32x4){pr[0], pr[1], pr[2], pr[3]};
+      xq[(2 * s + 1) * 64 + l] = (u32x4){pr[4], pr[5], pr[6], pr[7]};
+      // a kilobyte piece is four consecutive chunks, held by the four lanes
+      // of a DPP quad (chunk index = lane index mod 4): sum them there
+      float qs = sum + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                           __builtin_bit_cast(int, sum), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+      qs += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                __builtin_bit_cast(int, qs), 0x4E, 0xF, 0xF, false));            // quad_perm 2,3,0,1
+      if (c < 256 * A) {
+        if ((c & 3) == 0) xsum[(c >> 8) * 64 + l] = qs;
+      } else {
+        xsum[(A + ((c - 256 * A) >> 6)) * 64 + l] = sum;
       }
     }
   }
   __syncthreads();
+  if (stager) load_first();
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 3. the lane's pieces, as binary16 pairs (weights (e, e+8) of each
-  // dword) and their sums
-  auto load_act = [&](int64_t idx, float v[16]) {
-    const u32x4 *q = reinterpret_cast<const u32x4 *>(xl + idx);
-    const u32x4 a0 = q[0], a1 = q[1];
-    const uint32_t w[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[2 * i] = f16_to_f32((uint16_t)(w[i] & 0xFFFF));
-      v[2 * i + 1] = f16_to_f32((uint16_t)(w[i] >> 16));
-    }
-  };
-  half2_t xp[4 * A + BQ][8];
+  // ---- 3. the lane's activation pairs and piece sums
+  half2_t xp[NB][8];
   float xs[NP];
-  {
 #pragma unroll
-    for (int i = 0; i < A; ++i) {
-      float v[64];
+  for (int s = 0; s < NB; ++s) {
+    const u32x4 a = xq[(2 * s) * 64 + lane], b = xq[(2 * s + 1) * 64 + lane];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) load_act(4096 * i + 64 * lane + 16 * q, v + 16 * q);
-      float sum = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 64; ++q) sum += v[q];
-      xs[i] = sum;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xp[4 * i + d][e] = pack_h2(v[16 * d + e], v[16 * d + e + 8]);
-    }
-#pragma unroll
-    for (int j = 0; j < BQ; ++j) {
-      float v[16];
-      load_act(4096 * A + 1024 * j + 16 * lane, v);
-      float sum = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) sum += v[q];
-      xs[A + j] = sum;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xp[4 * A + j][e] = pack_h2(v[e], v[e + 8]);
+    for (int k = 0; k < 4; ++k) {
+      xp[s][k] = bits_h2(a[k]);
+      xp[s][4 + k] = bits_h2(b[k]);
     }
   }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- 4. the first D weight rows, only now: once a CU's memory queue fills
-  // with row loads, a wave stalls at its next load issue until rows arrive,
-  // and the short set-up above would wait for the weight stream
-  WRaw<A, BQ> ring[D];
-  const int gw32 = (int)gw, W32 = (int)W;
-  const int first = gw32 * D < n32 ? gw32 * D : n32 - 1;
 #pragma unroll
-  for (int d = 0; d < D; ++d) load_row(gw32 * D + d, first, ring[d]);
+  for (int pc = 0; pc < NP; ++pc) xs[pc] = xsum[pc * 64 + lane];
   __builtin_amdgcn_sched_barrier(0);
 
-  for (int base = gw32 * D; base < n32; base += D * W32) {
+  // ---- 4. passes of D rows
+  auto do_pass = [&](int base, auto refill) {
     float part[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
@@ -794,13 +821,17 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
       }
       part[d] = acc;
       // refill the slot with its row of the next pass
-      load_row(base + d + D * W32, base + d < n32 ? base + d : n32 - 1, ring[d]);
+      if constexpr (decltype(refill)::value)
+        load_row(base + d + D * W32, base + d < n32 ? base + d : n32 - 1, ring[d]);
       __builtin_amdgcn_sched_barrier(0);
     }
     int r;
     const float tot = rows8_sum<D>(part, lane, r);
-    if ((lane & 7) == 7 && r < D && base + r < p.n) y[base + r] = tot;
-  }
+    if ((lane & 7) == 7 && r < D && base + r < n32) y[base + r] = tot;
+  };
+  int base = gw32 * D;
+  for (; base + D * W32 < n32; base += D * W32) do_pass(base, std::integral_constant<bool, true>{});
+  if (base < n32) do_pass(base, std::integral_constant<bool, false>{});
 }
 
 template <int A, int BQ, int D, int XD, bool FUSED, int WPG>

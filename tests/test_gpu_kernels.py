@@ -193,6 +193,31 @@ def test_gemv_integer_exact_and_deterministic(fmt):
     assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("n,k", [(40000, 2048), (40000, 5120), (3001, 11264)])
+def test_gemv_batch1_multi_pass_integer_exact(n, k):
+    """Batch-1 PQ2_0 rows over several passes of the persistent grid (and
+    the last, partial one), alone and fused with the transform: scales 1.0
+    and integer activations make every partial sum an exact integer."""
+    rng = np.random.default_rng(n + k)
+    trits = synth.trits_uniform(rng, n, k)
+    sb = np.full((n, k // 128), 0x3C00, np.uint16)
+    payload = tq.pack_rowsplit("PQ2_0_G128", trits, sb)
+    xi = rng.integers(-8, 9, size=(1, k)).astype(np.float32)
+    say("gemv batch 1 multi-pass n=%d k=%d" % (n, k))
+    pd = dev(torch, payload)
+    y = tq.gemv_rowsplit(pd, "PQ2_0_G128", n, k, x_dev(torch, xi, "f32"))
+    # fused: the unrotated input D.(H.z)/32 (multiples of 1/32, exact in
+    # fp32) rotates back to z exactly, so the fused step is integer-exact too
+    sign_bits = synth.sign_bits(rng, k)
+    xu = T.inverse(xi.astype(np.float64), T.bf16_bits_to_f64(sign_bits)).astype(np.float32)
+    yf = tq.rotated_gemv_rowsplit(pd, "PQ2_0_G128", n, k, x_dev(torch, xu, "f32"),
+                                  signs_dev(torch, sign_bits))
+    torch.cuda.synchronize()
+    expect = (xi.astype(np.int64) @ trits.T.astype(np.int64)).astype(np.float32)
+    assert np.array_equal(y.cpu().numpy(), expect)
+    assert np.array_equal(yf.cpu().numpy(), expect)
+
+
 @pytest.mark.parametrize("fmt", ["PQ2_0_G128", "PTQ1_0_G128"])
 def test_gemv_non_ternary_codes_follow_decode_arithmetic(fmt):
     n, k = 40, 1024
