@@ -62,6 +62,18 @@ __device__ __forceinline__ void dot2_first5(const uint32_t (&t)[8], const half2_
         "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]));
 }
 
+// The same for four classes: a[c] = t[c].lo*x[c].lo + t[c].hi*x[c].hi.
+__device__ __forceinline__ void dot2_first4(const uint32_t (&t)[8], const half2_t *x, float (&a)[4]) {
+  asm("v_dot2_f32_f16 %0, %4, %8, 0\n\t"
+      "v_dot2_f32_f16 %1, %5, %9, 0\n\t"
+      "v_dot2_f32_f16 %2, %6, %10, 0\n\t"
+      "v_dot2_f32_f16 %3, %7, %11, 0\n\t"
+      "s_nop 2"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+      : "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]),
+        "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+}
+
 // cache policy of a streaming (read-once) buffer load
 constexpr int CPOL_NT = 2;
 
@@ -589,11 +601,11 @@ __device__ __forceinline__ float rows8_sum(const float (&v)[D], int lane, int &r
 // ("staging" waves) stage it into LDS as binary16 pairs in the order the
 // decoder consumes them, lane-major so that every lane later reads its own
 // pairs with conflict-free 16-byte LDS reads, together with the sum of every
-// lane piece.  The other waves request their first D weight rows at once,
-// so the weight stream starts at the beginning of the kernel; the staging
-// waves request theirs after the staging barrier (a wave whose loads fill
-// the compute unit's memory queue stalls at its next load until rows
-// arrive, which would hold up the staging).
+// lane piece.  The other waves request their first D weight rows as soon
+// as the activations have arrived, so the weight stream runs while the
+// staging waves work; the staging waves request theirs once the staging is
+// done (a wave whose loads fill the compute unit's memory queue stalls at
+// its next load until rows arrive, which would hold up the staging).
 //
 // With FUSED set the kernel also performs the signed transform of its input
 // ([tensorsharp] §4.2: a projection input is rotated by H(D.x)/32 per
@@ -613,6 +625,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   // (a kilobyte piece) and 256A + 64j + l for s = 4A + j (a 256-byte piece).
   __shared__ __attribute__((aligned(16))) u32x4 xq[NB * 128];
   __shared__ float xsum[NP * 64];  // [piece][lane]: sum of the piece's binary16 activations
+  __shared__ uint32_t staged;      // staging waves done
   // the transform's per-wave scratch (staging waves only)
   __shared__ __attribute__((aligned(16))) float wsc[FUSED ? (NB < WPG ? NB : WPG) : 1][1024];
   const int lane = threadIdx.x & 63;
@@ -664,27 +677,26 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
     for (int d = 0; d < D; ++d) load_row(gw32 * D + d, first, ring[d]);
   };
 
-  // ---- 1. non-staging waves: first D rows now
-  if (!stager) load_first();
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- 2. staging waves: activations -> binary16 pairs in LDS.  Fused:
-  // wave w transforms blocks w, w + WPG, ... (chunks 64*block + lane);
-  // unfused: thread t converts chunks t, t + 64*WPG, ...  Items past the end
-  // re-read the last block or chunk, so the loads stay unconditional.
+  // ---- 1. the staging waves load the activations, and the workgroup
+  // waits for them before any weight row is requested: requested alongside
+  // the rows, they would queue behind the weight stream.  Fused: wave w
+  // transforms blocks w, w + WPG, ... (chunks 64*block + lane); unfused:
+  // thread t converts chunks t, t + 64*WPG, ...  Items past the end re-read
+  // the last block or chunk, so the loads stay unconditional.
+  constexpr int NI = FUSED ? (NB + WPG - 1) / WPG : (NB * 64 + 64 * WPG - 1) / (64 * WPG);
+  Raw16<XD> xraw[NI];
+  u32x4 sraw[FUSED ? NI : 1][2];
+  auto item = [&](int i) -> int64_t {  // first element of item i of this thread
+    if constexpr (FUSED) {
+      const int blk = wave + WPG * i < NB ? wave + WPG * i : NB - 1;
+      return (int64_t)blk * 1024 + 16 * lane;
+    } else {
+      const int c = (int)threadIdx.x + 64 * WPG * i;
+      return 16 * (int64_t)(c < NB * 64 ? c : NB * 64 - 1);
+    }
+  };
+  if (threadIdx.x == 0) staged = 0;
   if (stager) {
-    constexpr int NI = FUSED ? (NB + WPG - 1) / WPG : (NB * 64 + 64 * WPG - 1) / (64 * WPG);
-    Raw16<XD> xraw[NI];
-    u32x4 sraw[FUSED ? NI : 1][2];
-    auto item = [&](int i) -> int64_t {  // first element of item i of this thread
-      if constexpr (FUSED) {
-        const int blk = wave + WPG * i < NB ? wave + WPG * i : NB - 1;
-        return (int64_t)blk * 1024 + 16 * lane;
-      } else {
-        const int c = (int)threadIdx.x + 64 * WPG * i;
-        return 16 * (int64_t)(c < NB * 64 ? c : NB * 64 - 1);
-      }
-    };
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       load16_raw<XD>(x, item(i), xraw[i]);
@@ -694,6 +706,16 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
         sraw[i][1] = sp[1];
       }
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  }
+  __syncthreads();
+
+  // ---- 2. the other waves request their first D rows now
+  if (!stager) load_first();
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 3. staging waves: activations -> binary16 pairs in LDS
+  if (stager) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const bool mine = FUSED ? wave + WPG * i < NB : (int)threadIdx.x + 64 * WPG * i < NB * 64;
@@ -768,12 +790,31 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
         xsum[(A + ((c - 256 * A) >> 6)) * 64 + l] = sum;
       }
     }
+    // publish: the wave's LDS writes complete before the count (LDS
+    // operations only: a release fence would also wait for the global loads)
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    if (lane == 0) __hip_atomic_fetch_add(&staged, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
-  __syncthreads();
-  if (stager) load_first();
-  __builtin_amdgcn_sched_barrier(0);
+  // Every wave waits for all staging waves.  Not a workgroup barrier: the
+  // other waves may still be stalled issuing their rows, and the staging
+  // waves need not wait for that.  Each staging wave counts exactly once
+  // on every path, so the wait ends; the bound only guards against a
+  // defect turning into a hang.
+  {
+    constexpr uint32_t NSTG = NB < WPG ? NB : WPG;
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+      const uint32_t done = __builtin_amdgcn_readfirstlane(
+          __hip_atomic_load(&staged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+      if (done >= NSTG) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    // the pair reads below are issued only after the count was seen, and
+    // LDS executes them after the writes that preceded it
+    asm volatile("" ::: "memory");
+  }
 
-  // ---- 3. the lane's activation pairs and piece sums
+  // ---- 4. the lane's activation pairs and piece sums (read before the
+  // staging waves request their rows, which may stall at issue)
   half2_t xp[NB][8];
   float xs[NP];
 #pragma unroll
@@ -788,8 +829,10 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
 #pragma unroll
   for (int pc = 0; pc < NP; ++pc) xs[pc] = xsum[pc * 64 + lane];
   __builtin_amdgcn_sched_barrier(0);
+  if (stager) load_first();
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 4. passes of D rows
+  // ---- 5. passes of D rows
   auto do_pass = [&](int base, auto refill) {
     float part[D];
 #pragma unroll
@@ -801,22 +844,22 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
       for (int pc = 0; pc < NP; ++pc) {
         const int nd = pc < A ? 4 : 1;
         const int d0 = pc < A ? 4 * pc : 4 * A + (pc - A);
-        float a[5];
+        // codes 0-3 (and 8-11) in place, codes 4-7 (and 12-15) shifted
+        // down a byte: four slot classes, e and e+4 in class e
+        float a[4];
 #pragma unroll
         for (int q = 0; q < nd; ++q) {
-          const uint32_t w = ring[d].w[d0 + q], w10 = w >> 10;
+          const uint32_t w = ring[d].w[d0 + q], w8 = w >> 8;
           const uint32_t t[8] = {w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u,
-                                 w & 0x00C000C0u, w & 0x03000300u, w10 & 0x00030003u,
-                                 w10 & 0x000C000Cu, w10 & 0x00300030u};
-          if (q == 0) dot2_first5(t, xp[d0], a);
+                                 w & 0x00C000C0u, w8 & 0x00030003u, w8 & 0x000C000Cu,
+                                 w8 & 0x00300030u, w8 & 0x00C000C0u};
+          if (q == 0) dot2_first4(t, xp[d0], a);
 #pragma unroll
-          for (int e = q == 0 ? 5 : 0; e < 8; ++e) {
-            const int c = e < 5 ? e : e - 5;
-            a[c] = __builtin_amdgcn_fdot2(bits_h2(t[e]), xp[d0 + q][e], a[c], false);
-          }
+          for (int e = q == 0 ? 4 : 0; e < 8; ++e)
+            a[e & 3] = __builtin_amdgcn_fdot2(bits_h2(t[e]), xp[d0 + q][e], a[e & 3], false);
         }
         const float cx = a[0] * 16777216.0f + a[1] * 4194304.0f + a[2] * 1048576.0f +
-                         a[3] * 262144.0f + a[4] * 65536.0f;
+                         a[3] * 262144.0f;
         acc += f16_to_f32((uint16_t)ring[d].s[pc]) * (cx - xs[pc]);
       }
       part[d] = acc;
