@@ -1267,6 +1267,7 @@ int64_t gemv_max_k(int fmt) { return fmt == FMT_PQ2 ? 64 * 1024 : 32 * 1024; }
 hipError_t launch_gemv(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx,
                        float *y, int64_t ldy, hipStream_t st) {
   if (p.fmt == FMT_PTQ1) {
+    if (gemv_ptq1_fits(p)) return launch_gemv_ptq1(p, x, xd, batch, ldx, y, ldy, st);
     if (batch <= 1) return gemv_b1<FMT_PTQ1, 32>(p, x, xd, ldx, y, ldy, st);
     if (batch <= 2) return gemv_go<FMT_PTQ1, 32, 2, 4>(p, x, xd, batch, ldx, y, ldy, st);
     if (batch <= 4) return gemv_go<FMT_PTQ1, 32, 4, 2>(p, x, xd, batch, ldx, y, ldy, st);

@@ -34,6 +34,12 @@ hipError_t launch_gemm(const Planes &p, const uint16_t *x, int x_dtype,
 
 int64_t gemv_max_k(int fmt);
 
+// PTQ1_0 GEMV on the matrix cores (any batch, in passes of four rows):
+// shapes it covers, and the launch.
+bool gemv_ptq1_fits(const Planes &p);
+hipError_t launch_gemv_ptq1(const Planes &p, const void *x, int x_dtype, int64_t batch,
+                            int64_t ldx, float *y, int64_t ldy, hipStream_t stream);
+
 // Signed transform fused into the GEMV (one launch): supported shapes, and
 // the launch itself (x unrotated, signs bf16 +-1).
 bool rotated_gemv_fused(const Planes &p, int64_t batch);
