@@ -6,8 +6,8 @@ rounded to binary16) and the PQ2_0_G128 decode GEMV against the 17408 x 5120
 FFN gate/up weight planes, issued as the library's one-launch decode step
 (tq_rotated_gemv_rowsplit: the transform runs in every workgroup while its
 first weight rows are in flight).  Inputs are resident in HBM before the
-timed region.  Each step uses the next of 24 distinct weight copies
-(24 x 23.7 MB, more than twice the 256 MB Infinity Cache) so the weight
+timed region.  Each step uses the next of 23 distinct weight copies
+(23 x 23.7 MB, more than twice the 256 MB Infinity Cache) so the weight
 stream comes from HBM, and the steps are launched as one HIP graph so the
 host launch rate does not limit them.
 
@@ -16,7 +16,8 @@ roofline of the dominant kernel (the fused decode kernel: algorithmic bytes
 per launch over its mean launch time from HIP events on its stream), the oracle's CPU
 throughput on a bounded sample, and secondary figures for the other
 workloads (PTQ1_0 down projection at batch 1/4/8, the vocabulary head and
-embedding rows, and the prefill GEMM in TFLOP/s).
+embedding rows, and the prefill GEMM in TFLOP/s, beside the vendor BLAS on a
+plain fp16 GEMM of the same shape for context).
 """
 
 import argparse
@@ -313,10 +314,16 @@ def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream):
         gmean = event_timed(torch, lambda i: tq.gemm_rowsplit(p5, c5["fmt"], n5, k5, xr5,
                                                                   out=y5), 10)
         flops = 2.0 * x5.shape[0] * n5 * k5
+        # context only: the vendor BLAS on a plain fp16 GEMM of the same shape
+        # (dense binary16 weights, no decode), on the same box
+        wd = torch.randn((n5, k5), device=x5.device, dtype=torch.float16).t().contiguous()
+        tmean = event_timed(torch, lambda i: torch.matmul(xr5, wd), 10)
+        del wd
         res["cfg5_prefill_gemm"] = {"m": int(x5.shape[0]), "n": n5, "k": k5,
                                     "mean_launch_us": round(gmean * 1e6, 2),
                                     "tflops": round(flops / gmean / 1e12, 1),
                                     "mfma_frac": round(flops / gmean / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                                    "torch_matmul_fp16_same_shape_us": round(tmean * 1e6, 2),
                                     "wht_2048x5120_us": round(wmean * 1e6, 2),
                                     "wht_gbs": round(x5.numel() * 4 / wmean / 1e9, 1)}
     torch.cuda.synchronize()

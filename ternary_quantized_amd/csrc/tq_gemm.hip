@@ -319,7 +319,10 @@ __device__ __forceinline__ void gemm_pq2_tile(const Planes &p, const uint16_t *_
   const uint16_t *xsrc = X + (xrow_ok ? (m0 + xr) : 0) * ldx + HX * xq;
   // code loads (threads below 2*TN): row wr, codes [32*wh, 32*wh + 32) of a
   // step (8 bytes) and that row's group scale
-  const bool wthread = t < 2 * TN;
+  // (every thread loads codes when the tile is 256 wide: no branch, so the
+  // compiler keeps counting the loads in flight instead of waiting for all
+  // of them where a branch around a load would rejoin)
+  const bool wthread = 2 * TN >= 512 || t < 2 * TN;
   const int wr = wthread ? t >> 1 : 0, wh = t & 1;
   const bool wrow_ok = wthread && n0 + wr < p.n;
   const int64_t wrow = wrow_ok ? n0 + wr : 0;
@@ -402,21 +405,27 @@ __device__ __forceinline__ void gemm_pq2_tile(const Planes &p, const uint16_t *_
     const int buf = ph & 1;
     const _Float16 *As = lds2 + buf * STAGE;
     const _Float16 *Bs = As + TM * G2ROW;
-#pragma unroll
-    for (int ks = 0; ks < G2K / 16; ++ks) {
+    // operand fragments of slice ks+1 are read while slice ks is multiplied
+    half8_t a[2][FM], bf[2][FN];
+    auto frags = [&](int ks, int set) {
       const int kb = ks * 16 + 8 * (lane >> 5);
-      half8_t a[FM], bf[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        a[i] = *reinterpret_cast<const half8_t *>(As + (wm + 32 * i + (lane & 31)) * G2ROW + kb);
+        a[set][i] = *reinterpret_cast<const half8_t *>(As + (wm + 32 * i + (lane & 31)) * G2ROW + kb);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bf[j] = *reinterpret_cast<const half8_t *>(Bs + (wn + 32 * j + (lane & 31)) * G2ROW + kb);
+        bf[set][j] = *reinterpret_cast<const half8_t *>(Bs + (wn + 32 * j + (lane & 31)) * G2ROW + kb);
+    };
+    frags(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < G2K / 16; ++ks) {
+      if (ks + 1 < G2K / 16) frags(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bf[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks & 1][i], bf[ks & 1][j], acc[i][j],
+                                                             0, 0, 0);
       store_piece((ph + 1) & 1, (ph + 1) & 3, buf ^ 1, ks);
     }
     __syncthreads();
