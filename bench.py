@@ -299,7 +299,18 @@ def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream):
         mean = event_timed(torch, lambda i: tq.embed_rows_inverse(cps[i % 2], c4["fmt"], n4, k4,
                                                                    ids, s4, out=emb), 20)
         res["cfg4_embed_64_rows_us"] = round(mean * 1e6, 3)
-        del cps
+        # load-time step (a ranked next part): GGUF block stream -> planes of
+        # the same head (337.7 MB in, 337.7 MB out), and back
+        nblk = n4 * (k4 // 128) * 34
+        blk = torch.empty(nblk, dtype=torch.uint8, device=xr.device)
+        tq.planes_to_blocks(cps[0], c4["fmt"], n4, k4, out=blk)
+        tmean = event_timed(torch, lambda i: tq.blocks_to_planes(blk, c4["fmt"], n4, k4, out=cps[1]), 4)
+        bmean = event_timed(torch, lambda i: tq.planes_to_blocks(cps[1], c4["fmt"], n4, k4, out=blk), 4)
+        res["transcode_head_blocks_to_planes"] = {"us": round(tmean * 1e6, 1),
+                                                  "gbs": round((nblk + p4.size) / tmean / 1e9, 1)}
+        res["transcode_head_planes_to_blocks"] = {"us": round(bmean * 1e6, 1),
+                                                  "gbs": round((nblk + p4.size) / bmean / 1e9, 1)}
+        del cps, blk
         torch.cuda.empty_cache()
 
         # config 5: prefill 2048 x 5120 -> WHT (binary16 out) -> GEMM N=17408

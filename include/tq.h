@@ -126,7 +126,73 @@ tq_status tq_unpack_rowsplit(int32_t format, int64_t n, int64_t k,
                              uint16_t *host_scale_bits,
                              uint64_t *host_bad_codes);
 
+/* .ninfer v2 container ([ninfer-skill] §1): bytes 0-7 the magic
+ * "NINFER\0\2", bytes 8-15 the little-endian uint64 directory length
+ * json_bytes, then the compact UTF-8 JSON directory; the payload starts at
+ * align_up(16 + json_bytes, 4096) and object offsets are relative to it.
+ * Validation (all of it, in directory order): root members exactly
+ * {identity, objects}; identity exactly {model_id, weights_id}, both
+ * non-empty strings; a tensor exactly {name, kind, shape, format, layout,
+ * offset, bytes}, a resource exactly {name, kind, encoding, offset, bytes};
+ * kind "tensor" or "resource"; resource encoding "raw-bytes-v1"; a tensor's
+ * bytes equal to its encoded size ("tensor <name> stores N bytes; layout
+ * requires M"); offset >= the end of the previous object, a multiple of the
+ * alignment (256 for tensors, 1 for resources), and offset + bytes inside
+ * the payload; unique names ("duplicate object name: <name>").
+ * Readings where the page is silent: layouts are the four NInfer v3
+ * layouts ([ninfer-v3] §6.2); encoded sizes are known for
+ * row_split_k128_v1 with PQ2_0_G128 / PTQ1_0_G128 (the row-split geometry)
+ * and for contiguous_le_v1 with bf16, fp32, int32 (elements times size,
+ * rank 0 = one element); block_scale_k16_m128x4_v1 and row_scale_v1 give
+ * TQ_ERR_UNSUPPORTED; other names TQ_ERR_FORMAT ("unknown numeric format:
+ * <f>", "unknown layout: <l>"); "compact" means no whitespace outside JSON
+ * strings; shape entries and bytes are positive integers, offsets
+ * non-negative integers. */
+typedef struct {
+  int32_t kind;        /* 0 tensor, 1 resource */
+  int32_t rank;        /* tensors: number of shape entries (0..16) */
+  int64_t shape[16];
+  uint64_t offset;     /* payload-relative byte offset */
+  uint64_t bytes;
+  char name[256];      /* NUL-terminated */
+  char format[64];     /* tensors: the format; resources: the encoding */
+  char layout[64];     /* tensors only */
+} tq_container_object;
+
+/* Validate host_file (file_bytes bytes of a whole container in host memory)
+ * and return the payload's file offset and the number of directory objects
+ * (either output may be NULL).  Errors: TQ_ERR_FORMAT with the message of
+ * the first rule broken, TQ_ERR_UNSUPPORTED as above, TQ_ERR_ARG for a
+ * NULL file with file_bytes > 0. */
+tq_status tq_container_parse(const uint8_t *host_file, uint64_t file_bytes,
+                             uint64_t *payload_offset, int64_t *count);
+
+/* Directory entry `index` (in directory order) of a valid container. */
+tq_status tq_container_object_at(const uint8_t *host_file, uint64_t file_bytes,
+                                 int64_t index, tq_container_object *out);
+
 /* --------------------------------------------------------- device ----- */
+
+/* GGUF block stream -> row-split planes ([ninfer-skill] §3-§4).  blocks:
+ * one block per (row, group) in row-major order over the [n, k_pad] groups,
+ * block_bytes 34 for PQ2_0_G128 ([scale 2][base 32]) or 28 for PTQ1_0_G128
+ * ([base 24][high 2][scale 2]); blocks_bytes must equal
+ * n * groups_per_row * block_bytes and payload_bytes the layout size.  Every
+ * payload byte is written (the padding between planes is zero).  The two
+ * buffers must not overlap (TQ_ERR_ARG); payload 256-byte and blocks 8-byte
+ * aligned (TQ_ERR_ALIGN).  Errors: TQ_ERR_GEOMETRY for a size mismatch. */
+tq_status tq_blocks_to_planes(const uint8_t *blocks, uint64_t blocks_bytes,
+                              int32_t format, int64_t n, int64_t k,
+                              uint8_t *payload, uint64_t payload_bytes,
+                              void *stream);
+
+/* Row-split planes -> GGUF block stream: the exact inverse of
+ * tq_blocks_to_planes on the plane bytes. */
+tq_status tq_planes_to_blocks(const uint8_t *payload, uint64_t payload_bytes,
+                              int32_t format, int64_t n, int64_t k,
+                              uint8_t *blocks, uint64_t blocks_bytes,
+                              void *stream);
+
 
 /* Signed blockwise Walsh-Hadamard transform of `rows` rows of width k
  * ([tensorsharp] §4.2; [ninfer-v3] §8 hadamard_signs):

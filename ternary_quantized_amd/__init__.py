@@ -9,7 +9,8 @@ kernels of ``libtq.so``; if the library is missing, every call raises.
 Entry points (same names as the C ABI without the ``tq_`` prefix):
 ``geometry``, ``pack_rowsplit``, ``unpack_rowsplit``, ``hadamard_signed``,
 ``gemv_rowsplit``, ``gemm_rowsplit``, ``embed_rows_inverse``,
-``decode_rowsplit``.
+``decode_rowsplit``, ``rotated_gemv_rowsplit``, ``blocks_to_planes``,
+``planes_to_blocks``, ``container_parse``.
 """
 
 import ctypes
@@ -37,7 +38,8 @@ EXPORTS = (
     "tq_last_error", "tq_version", "tq_geometry_get", "tq_pack_rowsplit",
     "tq_unpack_rowsplit", "tq_hadamard_signed", "tq_gemv_rowsplit",
     "tq_gemm_rowsplit", "tq_embed_rows_inverse", "tq_decode_rowsplit",
-    "tq_rotated_gemv_rowsplit",
+    "tq_rotated_gemv_rowsplit", "tq_blocks_to_planes", "tq_planes_to_blocks",
+    "tq_container_parse", "tq_container_object_at",
 )
 
 
@@ -45,6 +47,13 @@ class TQError(RuntimeError):
     def __init__(self, status, message):
         super().__init__("tq status %d: %s" % (status, message))
         self.status = status
+
+
+class ContainerObject(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 16), ("offset", ctypes.c_uint64),
+                ("bytes", ctypes.c_uint64), ("name", ctypes.c_char * 256),
+                ("format", ctypes.c_char * 64), ("layout", ctypes.c_char * 64)]
 
 
 class Geometry(ctypes.Structure):
@@ -78,6 +87,10 @@ def lib():
                                          _i64, _vp],
             "tq_embed_rows_inverse": [_vp, _u64, _i32, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _vp],
             "tq_decode_rowsplit": [_vp, _u64, _i32, _i64, _i64, _vp, _i64, _vp, _vp, _vp],
+            "tq_blocks_to_planes": [_vp, _u64, _i32, _i64, _i64, _vp, _u64, _vp],
+            "tq_planes_to_blocks": [_vp, _u64, _i32, _i64, _i64, _vp, _u64, _vp],
+            "tq_container_parse": [_vp, _u64, ctypes.POINTER(_u64), ctypes.POINTER(_i64)],
+            "tq_container_object_at": [_vp, _u64, _i64, ctypes.POINTER(ContainerObject)],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -129,6 +142,27 @@ def unpack_rowsplit(fmt, n, k, payload):
     _check(lib().tq_unpack_rowsplit(_fmt(fmt), n, k, payload.ctypes.data, payload.size,
                                     values.ctypes.data, scales.ctypes.data, ctypes.byref(bad)))
     return values, scales, int(bad.value)
+
+
+def container_parse(data):
+    """Validate a whole .ninfer container (bytes-like, host memory); return
+    (payload_offset, objects) with one dict per directory entry."""
+    buf = np.frombuffer(bytes(data), dtype=np.uint8)
+    ptr = buf.ctypes.data if buf.size else None
+    off, cnt = _u64(0), _i64(0)
+    _check(lib().tq_container_parse(ptr, buf.size, ctypes.byref(off), ctypes.byref(cnt)))
+    objs = []
+    for i in range(cnt.value):
+        o = ContainerObject()
+        _check(lib().tq_container_object_at(ptr, buf.size, i, ctypes.byref(o)))
+        d = {"name": o.name.decode(), "offset": int(o.offset), "bytes": int(o.bytes)}
+        if o.kind == 0:
+            d.update(kind="tensor", shape=[int(o.shape[j]) for j in range(o.rank)],
+                     format=o.format.decode(), layout=o.layout.decode())
+        else:
+            d.update(kind="resource", encoding=o.format.decode())
+        objs.append(d)
+    return int(off.value), objs
 
 
 # ---------------------------------------------------------------- device ---
@@ -266,3 +300,30 @@ def decode_rowsplit(payload, fmt, n, k, rows):
                                     _fmt(fmt), n, k, rows.data_ptr(), count, values.data_ptr(),
                                     scales.data_ptr(), _stream(rows.device)))
     return values, scales
+
+
+def blocks_to_planes(blocks, fmt, n, k, out=None):
+    """Row-split payload (uint8 device tensor) of a GGUF block stream."""
+    torch = _torch()
+    _dev(blocks, "blocks")
+    g = geometry(fmt, n, k)
+    if out is None:
+        out = torch.empty(g["payload_bytes"], dtype=torch.uint8, device=blocks.device)
+    _check(lib().tq_blocks_to_planes(blocks.data_ptr(), blocks.numel() * blocks.element_size(),
+                                     _fmt(fmt), n, k, out.data_ptr(),
+                                     out.numel() * out.element_size(), _stream(blocks.device)))
+    return out
+
+
+def planes_to_blocks(payload, fmt, n, k, out=None):
+    """GGUF block stream (uint8 device tensor) of a row-split payload."""
+    torch = _torch()
+    _dev(payload, "payload")
+    g = geometry(fmt, n, k)
+    nbytes = n * g["groups_per_row"] * (34 if _fmt(fmt) == PQ2_0_G128 else 28)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=payload.device)
+    _check(lib().tq_planes_to_blocks(payload.data_ptr(), payload.numel() * payload.element_size(),
+                                     _fmt(fmt), n, k, out.data_ptr(),
+                                     out.numel() * out.element_size(), _stream(payload.device)))
+    return out

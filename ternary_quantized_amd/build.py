@@ -14,8 +14,9 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
 BUILD = os.path.join(HERE, "_build")
 
-HIP_SOURCES = ["tq_hadamard.hip", "tq_gemv.hip", "tq_gemv_ptq1.hip", "tq_gemm.hip"]
-HOST_SOURCES = ["tq_host.cpp"]
+HIP_SOURCES = ["tq_hadamard.hip", "tq_gemv.hip", "tq_gemv_ptq1.hip", "tq_gemm.hip",
+               "tq_transcode.hip"]
+HOST_SOURCES = ["tq_host.cpp", "tq_container.cpp"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -18,9 +18,12 @@
 #include <string>
 
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
 
+namespace tq {
+// Record the message of a failing status for tq_last_error (shared with the
+// other host sources of the library).
 tq_status fail(tq_status st, const char *fmt, ...) {
   char buf[512];
   va_list ap;
@@ -30,6 +33,10 @@ tq_status fail(tq_status st, const char *fmt, ...) {
   g_err = buf;
   return st;
 }
+}  // namespace tq
+
+namespace {
+using tq::fail;
 
 uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
@@ -388,6 +395,48 @@ tq_status tq_decode_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
   return device_status(tq::launch_decode(p, rows, count, values, scale_bits,
                                          (int64_t)g.k_pad, (hipStream_t)stream),
                        "tq_decode_rowsplit");
+}
+
+// Block stream <-> planes: shared validation, then one launch.
+static tq_status transcode(const uint8_t *src, uint8_t *dst, bool to_planes, uint64_t payload_bytes,
+                           uint64_t blocks_bytes, int32_t format, int64_t n, int64_t k,
+                           void *stream, const char *what) {
+  tq_geometry g;
+  tq_status st = geometry(format, n, k, &g);
+  if (st != TQ_OK) return st;
+  if ((st = check_payload_size(g, payload_bytes)) != TQ_OK) return st;
+  const uint64_t blk = format == TQ_PQ2_0_G128 ? 34 : 28;
+  const uint64_t need = g.n * g.groups_per_row * blk;
+  if (blocks_bytes != need)
+    return fail(TQ_ERR_GEOMETRY, "block stream stores %llu bytes; layout requires %llu",
+                (unsigned long long)blocks_bytes, (unsigned long long)need);
+  if (!src || !dst) return fail(TQ_ERR_ARG, "blocks and payload must be non-NULL");
+  const uint8_t *payload = to_planes ? dst : src;
+  const uint8_t *blocks = to_planes ? src : dst;
+  if (!aligned(payload, kPlaneAlign))
+    return fail(TQ_ERR_ALIGN, "payload must be 256-byte aligned (plane alignment)");
+  if (!aligned(blocks, 8)) return fail(TQ_ERR_ALIGN, "blocks must be 8-byte aligned");
+  if (payload < blocks + blocks_bytes && blocks < payload + payload_bytes)
+    return fail(TQ_ERR_ARG, "blocks and payload overlap");
+  return device_status(tq::launch_transcode(format, to_planes, src, dst, g.base_bytes,
+                                            g.high_offset, g.high_bytes, g.scale_offset,
+                                            g.scale_bytes, g.payload_bytes, need,
+                                            (hipStream_t)stream),
+                       what);
+}
+
+tq_status tq_blocks_to_planes(const uint8_t *blocks, uint64_t blocks_bytes, int32_t format,
+                              int64_t n, int64_t k, uint8_t *payload, uint64_t payload_bytes,
+                              void *stream) {
+  return transcode(blocks, payload, true, payload_bytes, blocks_bytes, format, n, k, stream,
+                   "tq_blocks_to_planes");
+}
+
+tq_status tq_planes_to_blocks(const uint8_t *payload, uint64_t payload_bytes, int32_t format,
+                              int64_t n, int64_t k, uint8_t *blocks, uint64_t blocks_bytes,
+                              void *stream) {
+  return transcode(payload, blocks, false, payload_bytes, blocks_bytes, format, n, k, stream,
+                   "tq_planes_to_blocks");
 }
 
 }  // extern "C"

@@ -53,6 +53,12 @@ hipError_t launch_embed(const Planes &p, const int32_t *ids, int64_t count,
                         const uint16_t *signs, float *out, int64_t ldo,
                         int32_t *err_word, hipStream_t stream);
 
+// Block stream <-> planes (to_planes: src = blocks, dst = payload).
+hipError_t launch_transcode(int fmt, bool to_planes, const uint8_t *src, uint8_t *dst,
+                            uint64_t base_bytes, uint64_t high_offset, uint64_t high_bytes,
+                            uint64_t scale_offset, uint64_t scale_bytes, uint64_t payload_bytes,
+                            uint64_t blocks_bytes, hipStream_t stream);
+
 hipError_t launch_decode(const Planes &p, const int32_t *rows, int64_t count,
                          int8_t *values, uint16_t *scale_bits, int64_t k_pad,
                          hipStream_t stream);
