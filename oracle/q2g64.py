@@ -21,7 +21,11 @@ Readings (the pages leave these open):
 * the stream is row-major: row r holds blocks r*B .. r*B + B - 1 with
   B = k_pad / 64; block 2g and 2g + 1 of a row carry the two halves of the
   128-weight group g and both take that group's scale;
-* weights past k up to k_pad are trit 0 (code 1), as in the planes.
+* weights past k up to k_pad are trit 0 (code 1), as in the planes;
+* a stored value that is not a trit (a PQ2_0 code 3, which decodes to +2, or
+  a PTQ1_0 byte beyond the digit range, decoded by the digit arithmetic) is
+  carried over as its decoded value: the 2-bit code 3 also means +2, so the
+  expansion keeps every decoded value, ternary or not.
 """
 
 import numpy as np
@@ -36,6 +40,11 @@ GROUP = 128
 
 def blocks_per_row(k):
     return align_up(k, GROUP) // BLOCK_WEIGHTS
+
+
+def expanded_bytes(n, k):
+    """Size of the expanded stream of an n x k matrix."""
+    return n * blocks_per_row(k) * BLOCK_BYTES
 
 
 def expanded_bytes(n, k):
@@ -65,8 +74,6 @@ def expand(fmt, n, k, payload):
     two blocks with the group's scale, so no value changes.
     """
     vals, scale_bits = unpack_rowsplit(fmt, n, k, payload)
-    if vals.size and (vals.min() < -1 or vals.max() > 1):
-        raise ValueError("payload holds a code that is not a trit")
     nb = blocks_per_row(k)
     codes = (vals.astype(np.int32) + 1).reshape(n, nb, 16, 4)
     qs = (codes[..., 0] | (codes[..., 1] << 2) | (codes[..., 2] << 4) | (codes[..., 3] << 6))

@@ -102,14 +102,18 @@ def test_single_weight_positions():
         assert np.count_nonzero(blocks[:, 2:] != 0x55) == 1
 
 
-def test_rejects_non_ternary_payload():
-    n, k = 1, 128
-    payload = codec.pack_rowsplit("PQ2_0_G128", np.zeros((n, k), np.int8),
-                                  np.full((n, 1), 0x3C00, np.uint16))
-    payload = payload.copy()
-    payload[0] = 0xFF  # code 3 is not a trit
-    with pytest.raises(ValueError):
-        q2g64.expand("PQ2_0_G128", n, k, payload)
+@pytest.mark.parametrize("fmt,byte", [("PQ2_0_G128", 0xFF), ("PTQ1_0_G128", 0xFF)])
+def test_non_ternary_values_kept(fmt, byte):
+    # PQ2_0 code 3 decodes to +2 and a PTQ1_0 byte past 242 by the digit
+    # arithmetic; the 2-bit block keeps the decoded value either way
+    n, k = 2, 256
+    sb = np.full((n, 2), 0x3C00, np.uint16)
+    payload = codec.pack_rowsplit(fmt, np.zeros((n, k), np.int8), sb).copy()
+    payload[0] = byte
+    w = q2g64.dequantize(q2g64.expand(fmt, n, k, payload), n, k)
+    assert np.array_equal(w, P.dequantize(fmt, n, k, payload))
+    if fmt == "PQ2_0_G128":
+        assert list(w[0, :4]) == [2.0] * 4
 
 
 def test_projection_equals_plane_projection():
