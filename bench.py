@@ -192,7 +192,7 @@ def main():
         two_launch_us = (time.perf_counter() - t0) * 1e6 / args.steps
         del g2
     achieved = step_bytes / step_mean / 1e9
-    counters = load_counters("rotated_gemv_pq2_17408x5120_b1_counters.json", "tq_gemv.hip")
+    counters = load_counters("rotated_gemv_pq2_17408x5120_b1_counters.json", "tq_gemv_wave.h")
     traffic = None
     if counters:
         traffic = counters["hbm_bytes_per_dispatch"]
@@ -274,7 +274,45 @@ def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream):
             res["cfg3_ptq1_down_b%d" % b] = {"mean_launch_us": round(mean * 1e6, 3),
                                              "gbs": round(byts / mean / 1e9, 1),
                                              "frac_hbm": round(byts / mean / 1e9 / HBM_PEAK_GBS, 4)}
+        # the same matrix expanded losslessly to 2-bit G64 blocks (+29% bytes,
+        # codes without radix-3 digits), batch 1, and the expansion itself
+        gbytes = tq.g64_bytes(n3, k3)
+        gcps = [torch.empty(gbytes, dtype=torch.uint8, device=x3.device) for _ in range(copies_for(gbytes))]
+        for g in gcps:
+            tq.expand_g64(cps[0], c3["fmt"], n3, k3, out=g)
+        emean = event_timed(torch, lambda i: tq.expand_g64(cps[i % nc], c3["fmt"], n3, k3,
+                                                            out=gcps[i % len(gcps)]), 4 * nc)
         del cps
+        xr = tq.hadamard_signed(x3[:1], s3, out_dtype=torch.float16)
+        yb = torch.empty((1, n3), dtype=torch.float32, device=xr.device)
+        ng = len(gcps)
+        mean = event_timed(torch, lambda i: tq.gemv_g64(gcps[i % ng], n3, k3, xr, out=yb), 4 * ng)
+        byts = gbytes + 2 * k3 + 4 * n3
+        res["cfg3_expanded_g64_b1"] = {"bytes": gbytes, "mean_launch_us": round(mean * 1e6, 3),
+                                       "gbs": round(byts / mean / 1e9, 1),
+                                       "frac_hbm": round(byts / mean / 1e9 / HBM_PEAK_GBS, 4),
+                                       "expand_us": round(emean * 1e6, 2),
+                                       "expand_gbs": round((p3.size + gbytes) / emean / 1e9, 1)}
+        del gcps
+        torch.cuda.empty_cache()
+
+        # config 2 shape expanded to G64 (+6% bytes over PQ2_0), batch 1
+        c2 = synth.make_config(2)
+        p2 = to_dev(tq.pack_rowsplit(c2["fmt"], c2["trits"], c2["scale_bits"]))
+        n2, k2 = c2["n"], c2["k"]
+        gbytes = tq.g64_bytes(n2, k2)
+        gcps = [tq.expand_g64(p2, c2["fmt"], n2, k2) for _ in range(copies_for(gbytes))]
+        x2 = bits_dev(c2["x"], torch.bfloat16)
+        s2 = bits_dev(c2["sign_bits"], torch.bfloat16)
+        xr = tq.hadamard_signed(x2, s2, out_dtype=torch.float16)
+        yb = torch.empty((1, n2), dtype=torch.float32, device=xr.device)
+        ng = len(gcps)
+        mean = event_timed(torch, lambda i: tq.gemv_g64(gcps[i % ng], n2, k2, xr, out=yb), 4 * ng)
+        byts = gbytes + 2 * k2 + 4 * n2
+        res["cfg2_expanded_g64_b1"] = {"bytes": gbytes, "mean_launch_us": round(mean * 1e6, 3),
+                                       "gbs": round(byts / mean / 1e9, 1),
+                                       "frac_hbm": round(byts / mean / 1e9 / HBM_PEAK_GBS, 4)}
+        del gcps, p2
         torch.cuda.empty_cache()
 
         # config 4: vocabulary head N=248320 K=5120 batch 1 + 64 embedding rows
@@ -310,7 +348,13 @@ def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream):
                                                   "gbs": round((nblk + p4.size) / tmean / 1e9, 1)}
         res["transcode_head_planes_to_blocks"] = {"us": round(bmean * 1e6, 1),
                                                   "gbs": round((nblk + p4.size) / bmean / 1e9, 1)}
-        del cps, blk
+        del blk
+        gbytes = tq.g64_bytes(n4, k4)
+        g4 = torch.empty(gbytes, dtype=torch.uint8, device=xr.device)
+        emean = event_timed(torch, lambda i: tq.expand_g64(cps[i % 2], c4["fmt"], n4, k4, out=g4), 4)
+        res["expand_head_pq2_to_g64"] = {"us": round(emean * 1e6, 1),
+                                         "gbs": round((p4.size + gbytes) / emean / 1e9, 1)}
+        del cps, g4
         torch.cuda.empty_cache()
 
         # config 5: prefill 2048 x 5120 -> WHT (binary16 out) -> GEMM N=17408

@@ -193,6 +193,37 @@ tq_status tq_planes_to_blocks(const uint8_t *payload, uint64_t payload_bytes,
                               uint8_t *blocks, uint64_t blocks_bytes,
                               void *stream);
 
+/* 2-bit G64 block stream: the lossless expansion a runtime without the
+ * ternary types uses ([tensorsharp] §4.1: blocks expanded, not requantised,
+ * into the upstream 2-bit type, about +6% memory over PQ2_0 and +29% over
+ * PTQ1_0).  Layout (a reading: [gguf-explainer] §4.3 gives the code rule,
+ * [ninfer-v3] §6.1 the q2_g64_fp16 codec): row-major [n][k_pad/64] blocks
+ * of 18 bytes, each [binary16 d, little-endian][16 code bytes]; weight j of
+ * a block is code byte j/4, bits 2*(j%4), value (code-1)*d.  Blocks 2g and
+ * 2g+1 of a row hold group g's 128 weights, both with its scale. */
+
+/* *bytes = n * (k_pad/64) * 18.  Errors: TQ_ERR_SHAPE unless n, k >= 1,
+ * TQ_ERR_ARG for a NULL `bytes`. */
+tq_status tq_g64_bytes(int64_t n, int64_t k, uint64_t *bytes);
+
+/* Row-split planes (either format, validated as for tq_gemv_rowsplit) ->
+ * the G64 block stream `blocks` (exactly tq_g64_bytes bytes, 16-byte
+ * aligned, not overlapping the payload).  Every decoded value is kept: a
+ * PQ2_0 code 3 stays code 3 (+2) and a PTQ1_0 byte decodes by the digit
+ * arithmetic.  Errors: TQ_ERR_GEOMETRY for either size, TQ_ERR_ALIGN,
+ * TQ_ERR_ARG. */
+tq_status tq_expand_g64(const uint8_t *payload, uint64_t payload_bytes, int32_t format,
+                        int64_t n, int64_t k, uint8_t *blocks, uint64_t blocks_bytes,
+                        void *stream);
+
+/* Decode GEMV over the G64 block stream: y[n] = sum_j W[n][j] * xrot[j]
+ * with W as above; xrot and y as for tq_gemv_rowsplit (x rounded to
+ * binary16, fp32 accumulation).  Requirements: k % 1024 == 0 and
+ * k <= 17408 (TQ_ERR_SHAPE), n < 2^30, blocks 16-byte aligned.  Covered:
+ * batch 1; batch > 1 returns TQ_ERR_UNSUPPORTED with nothing enqueued. */
+tq_status tq_gemv_g64(const uint8_t *blocks, uint64_t blocks_bytes, int64_t n, int64_t k,
+                      const void *xrot, int32_t x_dtype, int64_t batch, int64_t ldx, float *y,
+                      int64_t ldy, void *stream);
 
 /* Signed blockwise Walsh-Hadamard transform of `rows` rows of width k
  * ([tensorsharp] §4.2; [ninfer-v3] §8 hadamard_signs):

@@ -39,7 +39,8 @@ EXPORTS = (
     "tq_unpack_rowsplit", "tq_hadamard_signed", "tq_gemv_rowsplit",
     "tq_gemm_rowsplit", "tq_embed_rows_inverse", "tq_decode_rowsplit",
     "tq_rotated_gemv_rowsplit", "tq_blocks_to_planes", "tq_planes_to_blocks",
-    "tq_container_parse", "tq_container_object_at",
+    "tq_container_parse", "tq_container_object_at", "tq_g64_bytes", "tq_expand_g64",
+    "tq_gemv_g64",
 )
 
 
@@ -91,6 +92,9 @@ def lib():
             "tq_planes_to_blocks": [_vp, _u64, _i32, _i64, _i64, _vp, _u64, _vp],
             "tq_container_parse": [_vp, _u64, ctypes.POINTER(_u64), ctypes.POINTER(_i64)],
             "tq_container_object_at": [_vp, _u64, _i64, ctypes.POINTER(ContainerObject)],
+            "tq_g64_bytes": [_i64, _i64, ctypes.POINTER(_u64)],
+            "tq_expand_g64": [_vp, _u64, _i32, _i64, _i64, _vp, _u64, _vp],
+            "tq_gemv_g64": [_vp, _u64, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _i64, _vp],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -326,4 +330,39 @@ def planes_to_blocks(payload, fmt, n, k, out=None):
     _check(lib().tq_planes_to_blocks(payload.data_ptr(), payload.numel() * payload.element_size(),
                                      _fmt(fmt), n, k, out.data_ptr(),
                                      out.numel() * out.element_size(), _stream(payload.device)))
+    return out
+
+
+def g64_bytes(n, k):
+    """Size of the 2-bit G64 block stream of an [n, k] matrix."""
+    out = _u64()
+    _check(lib().tq_g64_bytes(n, k, ctypes.byref(out)))
+    return int(out.value)
+
+
+def expand_g64(payload, fmt, n, k, out=None):
+    """2-bit G64 block stream (uint8 device tensor) of a row-split payload."""
+    torch = _torch()
+    _dev(payload, "payload")
+    if out is None:
+        out = torch.empty(g64_bytes(n, k), dtype=torch.uint8, device=payload.device)
+    _check(lib().tq_expand_g64(payload.data_ptr(), payload.numel() * payload.element_size(),
+                               _fmt(fmt), n, k, out.data_ptr(), out.numel() * out.element_size(),
+                               _stream(payload.device)))
+    return out
+
+
+def gemv_g64(blocks, n, k, xrot, out=None):
+    """y [batch, n] fp32 = decode-GEMV over a G64 block stream (batch 1)."""
+    torch = _torch()
+    _dev(blocks, "blocks")
+    _dev(xrot, "xrot")
+    if xrot.dim() == 1:
+        xrot = xrot.unsqueeze(0)
+    batch = xrot.shape[0]
+    if out is None:
+        out = torch.empty((batch, n), dtype=torch.float32, device=xrot.device)
+    _check(lib().tq_gemv_g64(blocks.data_ptr(), blocks.numel() * blocks.element_size(), n, k,
+                             xrot.data_ptr(), _dtype_code(xrot), batch, xrot.stride(0),
+                             out.data_ptr(), out.stride(0), _stream(xrot.device)))
     return out

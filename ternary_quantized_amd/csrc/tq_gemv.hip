@@ -22,9 +22,8 @@
 //    reproducible).
 
 #include "tq_device.h"
+#include "tq_gemv_wave.h"
 #include "tq_launch.h"
-
-#include <type_traits>
 
 namespace tq {
 
@@ -37,7 +36,6 @@ __device__ __forceinline__ half2_t cvt_codes(uint32_t v, int sel) {
   }
 }
 
-__device__ __forceinline__ half2_t bits_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 
 __device__ __forceinline__ float dot2(half2_t a, half2_t b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
@@ -62,20 +60,6 @@ __device__ __forceinline__ void dot2_first5(const uint32_t (&t)[8], const half2_
         "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]));
 }
 
-// The same for four classes: a[c] = t[c].lo*x[c].lo + t[c].hi*x[c].hi.
-__device__ __forceinline__ void dot2_first4(const uint32_t (&t)[8], const half2_t *x, float (&a)[4]) {
-  asm("v_dot2_f32_f16 %0, %4, %8, 0\n\t"
-      "v_dot2_f32_f16 %1, %5, %9, 0\n\t"
-      "v_dot2_f32_f16 %2, %6, %10, 0\n\t"
-      "v_dot2_f32_f16 %3, %7, %11, 0\n\t"
-      "s_nop 2"
-      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
-      : "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]),
-        "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
-}
-
-// cache policy of a streaming (read-once) buffer load
-constexpr int CPOL_NT = 2;
 
 __device__ __forceinline__ half2_t pack_h2(float a, float b) {
   half2_t r;
@@ -527,414 +511,12 @@ __global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restri
   }
 }
 
-// ---------------------------------------------------------------------------
-// PQ2_0 batch-1 GEMV, one wave per row.
-//
-// A row of k = 1024*m weights is k/4 bytes; lane l of the wave reads, for
-// each of the A = m/4 whole kilobytes of the row, the 16 bytes at
-// 1024*i + 16*l (64 weights, inside group 32*i + l/2) and, for each of the
-// BQ = m%4 remaining 256-byte blocks, the 4 bytes at 1024*A + 256*j + 4*l
-// (16 weights, inside group 32*A + 8*j + l/8).  Every load instruction of the
-// wave covers one contiguous span, the wave's partial sums are reduced with
-// DPP row shifts and four lane reads, and lane 0 writes the row: waves never
-// synchronise, so each is an independent persistent stream over blocks of D
-// consecutive rows (W = waves in the grid) with D rows in flight.
-template <int A, int BQ>
-struct WRaw {
-  uint32_t w[4 * A + BQ];
-  uint32_t s[A + BQ];
-};
-
-__device__ __forceinline__ float wave_sum(float v) {
-  v = seg_sum<16>(v);  // lanes 15, 31, 47, 63 hold their row's sum
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 15)) +
-         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31)) +
-         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 47)) +
-         __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-
-// Sums of up to 8 rows' per-lane partials v[0..D-1] over the 64 lanes of a
-// wave, all at once: two swap stages halve the values per lane while pairing
-// lane halves (32) and 16-lane rows, a rotate by 8 inside each 16-lane row
-// merges the last two values, and three DPP row shifts finish each 8-lane
-// group.  Lane 8g+7 then holds the total of row bitrev3(g); it is returned
-// for that lane (other lanes return garbage) together with the row index.
-template <int D>
-__device__ __forceinline__ float rows8_sum(const float (&v)[D], int lane, int &row) {
-  static_assert(D >= 1 && D <= 8, "at most 8 rows");
-  auto bits = [](float f) { return __builtin_bit_cast(unsigned, f); };
-  auto flt = [](unsigned u) { return __builtin_bit_cast(float, u); };
-  float u[8];
-#pragma unroll
-  for (int d = 0; d < 8; ++d) u[d] = d < D ? v[d] : 0.0f;
-  // lanes 0-31 | 32-63 of s1[i] carry rows 2i | 2i+1
-  float s1[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const auto r = __builtin_amdgcn_permlane32_swap(bits(u[2 * i]), bits(u[2 * i + 1]), false, false);
-    s1[i] = flt(r[0]) + flt(r[1]);
-  }
-  // 16-lane rows R0..R3 of s2[i] carry rows 4i + (0, 2, 1, 3)
-  float s2[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const auto r = __builtin_amdgcn_permlane16_swap(bits(s1[2 * i]), bits(s1[2 * i + 1]), false, false);
-    s2[i] = flt(r[0]) + flt(r[1]);
-  }
-  // lanes 0-7 of each 16-lane row keep s2[0], lanes 8-15 s2[1]; each adds
-  // the matching value of the other half-row (row_ror:8)
-  const bool hi = (lane & 8) != 0;
-  const float keep = hi ? s2[1] : s2[0];
-  const float give = hi ? s2[0] : s2[1];
-  float x = keep + flt(__builtin_amdgcn_update_dpp(0u, bits(give), 0x128, 0xF, 0xF, false));
-  x += flt(__builtin_amdgcn_update_dpp(0u, bits(x), 0x111, 0xF, 0xF, true));
-  x += flt(__builtin_amdgcn_update_dpp(0u, bits(x), 0x112, 0xF, 0xF, true));
-  x += flt(__builtin_amdgcn_update_dpp(0u, bits(x), 0x114, 0xF, 0xF, true));
-  const int g = lane >> 3;
-  row = ((g & 1) << 2) | (g & 2) | ((g >> 2) & 1);
-  return x;
-}
-
-// Workgroups are fat (WPG waves, one workgroup per CU) because the
-// activation row is read once per workgroup: every wave reading it on its own
-// sends thousands of requests to the same few L2 lines.  The first NB waves
-// ("staging" waves) stage it into LDS as binary16 pairs in the order the
-// decoder consumes them, lane-major so that every lane later reads its own
-// pairs with conflict-free 16-byte LDS reads, together with the sum of every
-// lane piece.  The other waves request their first D weight rows as soon
-// as the activations have arrived, so the weight stream runs while the
-// staging waves work; the staging waves request theirs once the staging is
-// done (a wave whose loads fill the compute unit's memory queue stalls at
-// its next load until rows arrive, which would hold up the staging).
-//
-// With FUSED set the kernel also performs the signed transform of its input
-// ([tensorsharp] §4.2: a projection input is rotated by H(D.x)/32 per
-// 1024-element block): x is then the unrotated activation row, each staging
-// wave transforms its 1024-element blocks in registers and rounds them to
-// binary16 exactly as the standalone transform with binary16 output does,
-// so one launch covers the whole step with the same result as two.
-template <int A, int BQ, int D, int XD, bool FUSED, int WPG>
-__global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const void *__restrict__ x,
-                                                             const uint16_t *__restrict__ signs,
-                                                             float *__restrict__ y) {
-  constexpr int NB = 4 * A + BQ;  // 1024-element blocks in a row = 16-weight dwords per lane
-  constexpr int NP = A + BQ;      // pieces per lane
-  // Activation pairs: dword s of lane l (16 weights, pairs (e, e+8)) is held
-  // by quads (2s)*64 + l (pairs 0-3) and (2s+1)*64 + l (pairs 4-7).  Dword s
-  // of lane l is natural 16-element chunk 256i + 4l + d for s = 4i + d < 4A
-  // (a kilobyte piece) and 256A + 64j + l for s = 4A + j (a 256-byte piece).
-  __shared__ __attribute__((aligned(16))) u32x4 xq[NB * 128];
-  __shared__ float xsum[NP * 64];  // [piece][lane]: sum of the piece's binary16 activations
-  __shared__ uint32_t staged;      // staging waves done
-  // the transform's per-wave scratch (staging waves only)
-  __shared__ __attribute__((aligned(16))) float wsc[FUSED ? (NB < WPG ? NB : WPG) : 1][1024];
-  const int lane = threadIdx.x & 63;
-  // the wave index is made explicitly uniform so that row offsets live in
-  // scalar registers and every load is (scalar row base + lane offset)
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t gw = (int64_t)blockIdx.x * WPG + wave;
-  const int64_t W = (int64_t)gridDim.x * WPG;
-  const bool stager = wave < NB;
-
-  // ---- rows: in pass q wave gw takes the D consecutive rows (q*W + gw)*D
-  // + d, so each wave streams one contiguous span of every plane; the launch
-  // picks D so that every wave has the same share.  Slot loads are
-  // unconditional: a branch around them would stop the compiler from
-  // counting the loads still in flight, and it would then wait for all of
-  // them at every row.  A slot whose next row lies past n re-reads the row
-  // it already holds (fb), so such loads stay spread over the planes; the
-  // last pass requests nothing (a wave cannot end before its loads return).
-  // Row numbers are 32-bit (the launch guarantees n < 2^30): the scalar
-  // unit has no 64-bit ordered compare, so 64-bit row tests would run on the
-  // vector unit every row.
-  const int n32 = (int)p.n;
-  const int q0 = lane / 2, q1 = 32 * A + lane / 8;  // scale entries
-  auto load_row = [&](int row, int fb, WRaw<A, BQ> &r) {
-    const int rr = row < n32 ? row : fb;
-    // the row's base bytes as a buffer: the row address stays in scalar
-    // registers and each load adds only the lane's offset (a streaming load
-    // through a flat pointer would rebuild the 64-bit address every row)
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(p.base + (int64_t)rr * p.base_row), 0, (int)p.base_row, 0x00020000);
-    const uint16_t *rs = p.scale + (int64_t)rr * p.groups;
-#pragma unroll
-    for (int i = 0; i < A; ++i) {
-      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane + 1024 * i, 0, CPOL_NT);
-      r.w[4 * i] = t[0]; r.w[4 * i + 1] = t[1]; r.w[4 * i + 2] = t[2]; r.w[4 * i + 3] = t[3];
-      r.s[i] = rs[q0 + 32 * i];
-    }
-#pragma unroll
-    for (int j = 0; j < BQ; ++j) {
-      r.w[4 * A + j] = __builtin_amdgcn_raw_buffer_load_b32(rb, 1024 * A + 4 * lane + 256 * j, 0, CPOL_NT);
-      r.s[A + j] = rs[q1 + 8 * j];
-    }
-  };
-  WRaw<A, BQ> ring[D];
-  const int gw32 = (int)gw, W32 = (int)W;
-  const int first = gw32 * D < n32 ? gw32 * D : n32 - 1;
-  auto load_first = [&]() {
-#pragma unroll
-    for (int d = 0; d < D; ++d) load_row(gw32 * D + d, first, ring[d]);
-  };
-
-  // ---- 1. the staging waves load the activations, and the workgroup
-  // waits for them before any weight row is requested: requested alongside
-  // the rows, they would queue behind the weight stream.  Fused: wave w
-  // transforms blocks w, w + WPG, ... (chunks 64*block + lane); unfused:
-  // thread t converts chunks t, t + 64*WPG, ...  Items past the end re-read
-  // the last block or chunk, so the loads stay unconditional.
-  constexpr int NI = FUSED ? (NB + WPG - 1) / WPG : (NB * 64 + 64 * WPG - 1) / (64 * WPG);
-  Raw16<XD> xraw[NI];
-  u32x4 sraw[FUSED ? NI : 1][2];
-  auto item = [&](int i) -> int64_t {  // first element of item i of this thread
-    if constexpr (FUSED) {
-      const int blk = wave + WPG * i < NB ? wave + WPG * i : NB - 1;
-      return (int64_t)blk * 1024 + 16 * lane;
-    } else {
-      const int c = (int)threadIdx.x + 64 * WPG * i;
-      return 16 * (int64_t)(c < NB * 64 ? c : NB * 64 - 1);
-    }
-  };
-  if (threadIdx.x == 0) staged = 0;
-  if (stager) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      load16_raw<XD>(x, item(i), xraw[i]);
-      if constexpr (FUSED) {
-        const u32x4 *sp = reinterpret_cast<const u32x4 *>(signs + item(i));
-        sraw[i][0] = sp[0];
-        sraw[i][1] = sp[1];
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  }
-  __syncthreads();
-
-  // ---- 2. the other waves request their first D rows now
-  if (!stager) load_first();
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- 3. staging waves: activations -> binary16 pairs in LDS
-  if (stager) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const bool mine = FUSED ? wave + WPG * i < NB : (int)threadIdx.x + 64 * WPG * i < NB * 64;
-      if (!mine) continue;
-      // h[m]: binary16 elements 2m, 2m+1 of this thread's 16-element chunk
-      uint32_t h[8];
-      if constexpr (FUSED) {
-        float v[16];
-        convert16<XD>(xraw[i], v);
-        const uint32_t sw[8] = {sraw[i][0][0], sraw[i][0][1], sraw[i][0][2], sraw[i][0][3],
-                                sraw[i][1][0], sraw[i][1][1], sraw[i][1][2], sraw[i][1][3]};
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          v[e] = apply_sign(v[e], (uint16_t)(sw[e >> 1] >> (16 * (e & 1))));
-        // v[4g + j] leaves the transform holding element 256g + 4*lane + j
-        // of the block; the block goes back through the wave's scratch in
-        // natural order, and the lane takes chunk `lane` of it
-        float *sc = wsc[wave];
-        wht1024_wave(v, lane, sc);
-        uint16_t *nat = reinterpret_cast<uint16_t *>(sc);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint32_t lo = (uint32_t)f32_to_f16(v[4 * g] * 0.03125f) |
-                              ((uint32_t)f32_to_f16(v[4 * g + 1] * 0.03125f) << 16);
-          const uint32_t hi = (uint32_t)f32_to_f16(v[4 * g + 2] * 0.03125f) |
-                              ((uint32_t)f32_to_f16(v[4 * g + 3] * 0.03125f) << 16);
-          *reinterpret_cast<u32x2 *>(nat + 256 * g + 4 * lane) = (u32x2){lo, hi};
-        }
-        const u32x4 *q = reinterpret_cast<const u32x4 *>(nat + 16 * lane);
-        const u32x4 a0 = q[0], a1 = q[1];
-        h[0] = a0[0]; h[1] = a0[1]; h[2] = a0[2]; h[3] = a0[3];
-        h[4] = a1[0]; h[5] = a1[1]; h[6] = a1[2]; h[7] = a1[3];
-      } else if constexpr (XD == DT_F16) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) { h[m] = xraw[i].q[0][m]; h[4 + m] = xraw[i].q[1][m]; }
-      } else {
-        float v[16];
-        convert16<XD>(xraw[i], v);
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-          h[m] = (uint32_t)f32_to_f16(v[2 * m]) | ((uint32_t)f32_to_f16(v[2 * m + 1]) << 16);
-      }
-      // pairs (e, e+8) of the chunk and their sum
-      uint32_t pr[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pr[e] = __builtin_amdgcn_perm(h[4 + e / 2], h[e / 2], (e & 1) ? 0x07060302u : 0x05040100u);
-      float sum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sum = __builtin_amdgcn_fdot2(bits_h2(pr[e]), bits_h2(0x3C003C00u), sum, false);
-      const int c = FUSED ? (wave + WPG * i) * 64 + lane : (int)threadIdx.x + 64 * WPG * i;
-      int s, l;
-      if (c < 256 * A) {
-        s = 4 * (c >> 8) + (c & 3);
-        l = (c & 255) >> 2;
-      } else {
-        s = 4 * A + ((c - 256 * A) >> 6);
-        l = (c - 256 * A) & 63;
-      }
-      xq[(2 * s) * 64 + l] = (u32x4){pr[0], pr[1], pr[2], pr[3]};
-      xq[(2 * s + 1) * 64 + l] = (u32x4){pr[4], pr[5], pr[6], pr[7]};
-      // a kilobyte piece is four consecutive chunks, held by the four lanes
-      // of a DPP quad (chunk index = lane index mod 4): sum them there
-      float qs = sum + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                           __builtin_bit_cast(int, sum), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
-      qs += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                __builtin_bit_cast(int, qs), 0x4E, 0xF, 0xF, false));            // quad_perm 2,3,0,1
-      if (c < 256 * A) {
-        if ((c & 3) == 0) xsum[(c >> 8) * 64 + l] = qs;
-      } else {
-        xsum[(A + ((c - 256 * A) >> 6)) * 64 + l] = sum;
-      }
-    }
-    // publish: the wave's LDS writes complete before the count (LDS
-    // operations only: a release fence would also wait for the global loads)
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    if (lane == 0) __hip_atomic_fetch_add(&staged, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  }
-  // Every wave waits for all staging waves.  Not a workgroup barrier: the
-  // other waves may still be stalled issuing their rows, and the staging
-  // waves need not wait for that.  Each staging wave counts exactly once
-  // on every path, so the wait ends; the bound only guards against a
-  // defect turning into a hang.
-  {
-    constexpr uint32_t NSTG = NB < WPG ? NB : WPG;
-    for (int spin = 0; spin < (1 << 22); ++spin) {
-      const uint32_t done = __builtin_amdgcn_readfirstlane(
-          __hip_atomic_load(&staged, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-      if (done >= NSTG) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
-    // the pair reads below are issued only after the count was seen, and
-    // LDS executes them after the writes that preceded it
-    asm volatile("" ::: "memory");
-  }
-
-  // ---- 4. the lane's activation pairs and piece sums (read before the
-  // staging waves request their rows, which may stall at issue)
-  half2_t xp[NB][8];
-  float xs[NP];
-#pragma unroll
-  for (int s = 0; s < NB; ++s) {
-    const u32x4 a = xq[(2 * s) * 64 + lane], b = xq[(2 * s + 1) * 64 + lane];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      xp[s][k] = bits_h2(a[k]);
-      xp[s][4 + k] = bits_h2(b[k]);
-    }
-  }
-#pragma unroll
-  for (int pc = 0; pc < NP; ++pc) xs[pc] = xsum[pc * 64 + lane];
-  __builtin_amdgcn_sched_barrier(0);
-  if (stager) load_first();
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- 5. passes of D rows
-  auto do_pass = [&](int base, auto refill) {
-    float part[D];
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      // sum over the lane's pieces of s * (sum code*x - sum x); the first
-      // product of each class starts from 0 instead of a zeroed register
-      float acc = 0.0f;
-#pragma unroll
-      for (int pc = 0; pc < NP; ++pc) {
-        const int nd = pc < A ? 4 : 1;
-        const int d0 = pc < A ? 4 * pc : 4 * A + (pc - A);
-        // codes 0-3 (and 8-11) in place, codes 4-7 (and 12-15) shifted
-        // down a byte: four slot classes, e and e+4 in class e
-        float a[4];
-#pragma unroll
-        for (int q = 0; q < nd; ++q) {
-          const uint32_t w = ring[d].w[d0 + q], w8 = w >> 8;
-          const uint32_t t[8] = {w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u,
-                                 w & 0x00C000C0u, w8 & 0x00030003u, w8 & 0x000C000Cu,
-                                 w8 & 0x00300030u, w8 & 0x00C000C0u};
-          if (q == 0) dot2_first4(t, xp[d0], a);
-#pragma unroll
-          for (int e = q == 0 ? 4 : 0; e < 8; ++e)
-            a[e & 3] = __builtin_amdgcn_fdot2(bits_h2(t[e]), xp[d0 + q][e], a[e & 3], false);
-        }
-        const float cx = a[0] * 16777216.0f + a[1] * 4194304.0f + a[2] * 1048576.0f +
-                         a[3] * 262144.0f;
-        acc += f16_to_f32((uint16_t)ring[d].s[pc]) * (cx - xs[pc]);
-      }
-      part[d] = acc;
-      // refill the slot with its row of the next pass
-      if constexpr (decltype(refill)::value)
-        load_row(base + d + D * W32, base + d < n32 ? base + d : n32 - 1, ring[d]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    int r;
-    const float tot = rows8_sum<D>(part, lane, r);
-    if ((lane & 7) == 7 && r < D && base + r < n32) y[base + r] = tot;
-  };
-  int base = gw32 * D;
-  for (; base + D * W32 < n32; base += D * W32) do_pass(base, std::integral_constant<bool, true>{});
-  if (base < n32) do_pass(base, std::integral_constant<bool, false>{});
-}
-
-template <int A, int BQ, int D, int XD, bool FUSED, int WPG>
-static hipError_t gemv_wave_launch(const Planes &p, const void *x, const uint16_t *signs, float *y,
-                                   int64_t waves, hipStream_t st) {
-  const int64_t grid = (waves + WPG - 1) / WPG;
-  hipLaunchKernelGGL((gemv_wave_kernel<A, BQ, D, XD, FUSED, WPG>), dim3((unsigned)grid),
-                     dim3(64 * WPG), 0, st, p, x, signs, y);
-  return hipGetLastError();
-}
-
-// Row split: for each ring depth D in {4, 6, 8} (D rows per wave and pass)
-// take as many workgroups per CU as fit, the fewest passes that cover n, and
-// then the fewest waves; keep the D whose busiest CU has the fewest rows
-// (ties: the deeper ring).  Rows past n in a wave's last block re-read the
-// row their slot already holds.  Workgroup size by register need: three
-// waves per SIMD up to k = 5120 (WPG 12), two up to k = 7168 (WPG 8), one
-// beyond (WPG 4).
-template <int A, int BQ, int XD, bool FUSED>
-static hipError_t gemv_wave_go(const Planes &p, const void *x, const uint16_t *signs, float *y,
-                               hipStream_t st) {
-  constexpr int NBK = 4 * A + BQ;
-  constexpr int WPG = NBK <= 5 ? 12 : NBK <= 7 ? 8 : 4;
-  const int cus = device_cus();
-  const void *kerns[3] = {
-      reinterpret_cast<const void *>(gemv_wave_kernel<A, BQ, 4, XD, FUSED, WPG>),
-      reinterpret_cast<const void *>(gemv_wave_kernel<A, BQ, 6, XD, FUSED, WPG>),
-      reinterpret_cast<const void *>(gemv_wave_kernel<A, BQ, 8, XD, FUSED, WPG>)};
-  const int depth[3] = {4, 6, 8};
-  int best = -1;
-  int64_t best_rows = 0, best_waves = 0;
-  for (int i = 0; i < 3; ++i) {
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kerns[i], 64 * WPG, 0) != hipSuccess ||
-        per_cu < 1)
-      continue;  // this depth does not fit a workgroup on a CU
-    const int64_t D = depth[i];
-    const int64_t slots = (int64_t)WPG * cus * per_cu;
-    const int64_t passes = (p.n + slots * D - 1) / (slots * D);
-    const int64_t waves = (p.n + D * passes - 1) / (D * passes);
-    const int64_t wgs = (waves + WPG - 1) / WPG;
-    const int64_t rows_cu = ((wgs + cus - 1) / cus) * WPG * D * passes;
-    if (best < 0 || rows_cu <= best_rows) {
-      best = i;
-      best_rows = rows_cu;
-      best_waves = waves;
-    }
-  }
-  if (best < 0) return hipErrorInvalidConfiguration;
-  if (best == 0) return gemv_wave_launch<A, BQ, 4, XD, FUSED, WPG>(p, x, signs, y, best_waves, st);
-  if (best == 1) return gemv_wave_launch<A, BQ, 6, XD, FUSED, WPG>(p, x, signs, y, best_waves, st);
-  return gemv_wave_launch<A, BQ, 8, XD, FUSED, WPG>(p, x, signs, y, best_waves, st);
-}
-
 template <int A, int BQ, bool FUSED>
 static hipError_t gemv_wave_dt(const Planes &p, const void *x, int xd, const uint16_t *signs,
                                float *y, hipStream_t st) {
-  if (xd == DT_F32) return gemv_wave_go<A, BQ, DT_F32, FUSED>(p, x, signs, y, st);
-  if (xd == DT_BF16) return gemv_wave_go<A, BQ, DT_BF16, FUSED>(p, x, signs, y, st);
-  return gemv_wave_go<A, BQ, DT_F16, FUSED>(p, x, signs, y, st);
+  if (xd == DT_F32) return gemv_wave_go<LAY_PLANES, A, BQ, DT_F32, FUSED>(p, x, signs, y, st);
+  if (xd == DT_BF16) return gemv_wave_go<LAY_PLANES, A, BQ, DT_BF16, FUSED>(p, x, signs, y, st);
+  return gemv_wave_go<LAY_PLANES, A, BQ, DT_F16, FUSED>(p, x, signs, y, st);
 }
 
 // k = 1024*m with m <= 11: pieces A = m/4 kilobytes + BQ = m%4 blocks.

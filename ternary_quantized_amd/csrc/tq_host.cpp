@@ -439,4 +439,66 @@ tq_status tq_planes_to_blocks(const uint8_t *payload, uint64_t payload_bytes, in
                    "tq_planes_to_blocks");
 }
 
+// 2-bit G64 block stream ([tensorsharp] §4.1 expansion; block rule of
+// [gguf-explainer] §4.3): n rows of k_pad/64 blocks of 18 bytes.
+static uint64_t g64_bytes(const tq_geometry &g) { return g.n * (g.k_pad / 64) * 18; }
+
+tq_status tq_g64_bytes(int64_t n, int64_t k, uint64_t *bytes) {
+  if (!bytes) return fail(TQ_ERR_ARG, "bytes is NULL");
+  tq_geometry g;
+  tq_status st = geometry(TQ_PQ2_0_G128, n, k, &g);
+  if (st != TQ_OK) return st;
+  *bytes = g64_bytes(g);
+  return TQ_OK;
+}
+
+tq_status tq_expand_g64(const uint8_t *payload, uint64_t payload_bytes, int32_t format,
+                        int64_t n, int64_t k, uint8_t *blocks, uint64_t blocks_bytes,
+                        void *stream) {
+  tq_geometry g;
+  tq::Planes p;
+  tq_status st = check_device_payload(payload, payload_bytes, format, n, k, &g, &p);
+  if (st != TQ_OK) return st;
+  const uint64_t need = g64_bytes(g);
+  if (blocks_bytes != need)
+    return fail(TQ_ERR_GEOMETRY, "block stream stores %llu bytes; layout requires %llu",
+                (unsigned long long)blocks_bytes, (unsigned long long)need);
+  if (!blocks) return fail(TQ_ERR_ARG, "blocks is NULL");
+  if (!aligned(blocks, 16)) return fail(TQ_ERR_ALIGN, "blocks must be 16-byte aligned");
+  if (payload < blocks + blocks_bytes && blocks < payload + payload_bytes)
+    return fail(TQ_ERR_ARG, "blocks and payload overlap");
+  return device_status(tq::launch_expand_g64(format, p.base, p.high, p.scale, blocks,
+                                             (int64_t)(g.n * g.groups_per_row),
+                                             (hipStream_t)stream),
+                       "tq_expand_g64");
+}
+
+tq_status tq_gemv_g64(const uint8_t *blocks, uint64_t blocks_bytes, int64_t n, int64_t k,
+                      const void *xrot, int32_t x_dtype, int64_t batch, int64_t ldx, float *y,
+                      int64_t ldy, void *stream) {
+  tq_geometry g;
+  tq_status st = geometry(TQ_PQ2_0_G128, n, k, &g);
+  if (st != TQ_OK) return st;
+  const uint64_t need = g64_bytes(g);
+  if (blocks_bytes != need)
+    return fail(TQ_ERR_GEOMETRY, "block stream stores %llu bytes; layout requires %llu",
+                (unsigned long long)blocks_bytes, (unsigned long long)need);
+  if (k % 1024 || k > 17 * 1024)
+    return fail(TQ_ERR_SHAPE, "k=%lld: the G64 GEMV needs k %% 1024 == 0 and k <= 17408",
+                (long long)k);
+  if (n >= (int64_t(1) << 30)) return fail(TQ_ERR_SHAPE, "n=%lld must be below 2^30", (long long)n);
+  if (batch < 1) return fail(TQ_ERR_SHAPE, "batch=%lld must be >= 1", (long long)batch);
+  if (!dtype_ok(x_dtype)) return fail(TQ_ERR_ARG, "x_dtype must be TQ_F32, TQ_BF16 or TQ_F16");
+  if (!blocks || !xrot || !y) return fail(TQ_ERR_ARG, "blocks, xrot and y must be non-NULL");
+  if (ldx < k || ldy < n) return fail(TQ_ERR_ARG, "ldx must be >= k and ldy >= n");
+  if (!aligned(blocks, 16)) return fail(TQ_ERR_ALIGN, "blocks must be 16-byte aligned");
+  if (!aligned(xrot, 16) || ldx % 8)
+    return fail(TQ_ERR_ALIGN, "xrot must be 16-byte aligned with ldx a multiple of 8");
+  if (!aligned(y, 4)) return fail(TQ_ERR_ALIGN, "y must be 4-byte aligned");
+  if (batch != 1)
+    return fail(TQ_ERR_UNSUPPORTED, "the G64 GEMV covers batch 1 only (got %lld)", (long long)batch);
+  return device_status(tq::launch_gemv_g64(blocks, n, k, xrot, x_dtype, y, (hipStream_t)stream),
+                       "tq_gemv_g64");
+}
+
 }  // extern "C"

@@ -59,6 +59,17 @@ hipError_t launch_transcode(int fmt, bool to_planes, const uint8_t *src, uint8_t
                             uint64_t scale_offset, uint64_t scale_bytes, uint64_t payload_bytes,
                             uint64_t blocks_bytes, hipStream_t stream);
 
+// Planes -> 2-bit G64 block stream (one thread per 128-weight group; the
+// plane pointers are at their offsets, `groups` = n * groups_per_row).
+hipError_t launch_expand_g64(int fmt, const uint8_t *base, const uint8_t *high,
+                             const uint16_t *scale, uint8_t *out, int64_t groups,
+                             hipStream_t st);
+
+// Batch-1 GEMV over the G64 block stream ([n][k/64] blocks of 18 bytes),
+// k = 1024*m with 1 <= m <= 17, n < 2^30.
+hipError_t launch_gemv_g64(const uint8_t *blocks, int64_t n, int64_t k, const void *x, int x_dtype,
+                           float *y, hipStream_t st);
+
 hipError_t launch_decode(const Planes &p, const int32_t *rows, int64_t count,
                          int8_t *values, uint16_t *scale_bits, int64_t k_pad,
                          hipStream_t stream);
