@@ -332,6 +332,18 @@ def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream):
         res["cfg4_head_b1"] = {"mean_launch_us": round(mean * 1e6, 3),
                                "gbs": round(byts / mean / 1e9, 1),
                                "frac_hbm": round(byts / mean / 1e9 / HBM_PEAK_GBS, 4)}
+        # the whole head step in one launch: RMSNorm, transform, head GEMV and
+        # the greedy token (the logits are written too)
+        gnorm = bits_dev(synth.norm_weight_bits(np.random.default_rng(44), k4), torch.bfloat16)
+        work = torch.zeros(2, dtype=torch.int64, device=xr.device)
+        tok = torch.empty(1, dtype=torch.int32, device=xr.device)
+        hmean = event_timed(torch, lambda i: tq.head_argmax(cps[i % 2], c4["fmt"], n4, k4, x4, gnorm,
+                                                             1e-6, s4, work, logits=y4[0], token=tok),
+                            20)
+        hbytes = p4.size + 3 * 2 * k4 + 4 * n4 + 4
+        res["cfg4_head_greedy_one_launch"] = {"mean_launch_us": round(hmean * 1e6, 3),
+                                              "gbs": round(hbytes / hmean / 1e9, 1),
+                                              "frac_hbm": round(hbytes / hmean / 1e9 / HBM_PEAK_GBS, 4)}
         ids = to_dev(c4["ids"])
         emb = torch.empty((64, k4), dtype=torch.float32, device=xr.device)
         mean = event_timed(torch, lambda i: tq.embed_rows_inverse(cps[i % 2], c4["fmt"], n4, k4,

@@ -278,6 +278,30 @@ tq_status tq_rotated_gemv_rowsplit(const uint8_t *payload, uint64_t payload_byte
                                    int64_t ldx, const uint16_t *signs_bf16,
                                    float *y, int64_t ldy, void *stream);
 
+/* Output head of a decode step in one launch ([tensorsharp] §4.4: after the
+ * last layer, RMSNorm, the signed Hadamard transform and the low-bit output
+ * head give the logits) with the greedy choice fused in (a GEMV that also
+ * finds the argmax: [gguf-explainer] §4.5):
+ *   r = x * g / sqrt(mean_j(x_j^2) + eps)        (RMSNorm; a reading: the
+ *       pages name the step, not its formula; g = norm_bf16 [k], eps >= 0)
+ *   xrot = binary16( H (d . r) / 32 )  per 1024-element block
+ *   logits[n] = sum_g s[n][g] * sum_{j in g} t[n][j] * xrot[j]
+ *   *token = the lowest index among the largest logits (-0 equals +0).
+ * x: one hidden row, x_dtype F32, BF16 or F16, 16-byte aligned; the sum of
+ * squares and the scale are fp32.  logits: fp32 [n], or NULL to skip them.
+ * work: two uint64 words of device memory, 16-byte aligned, owned by the
+ * caller, zero before the first call; every call leaves them zero again.
+ * Calls that share a work buffer must not run concurrently.  token: one
+ * device int32 (-1 if no logit is ordered, i.e. all are NaN).
+ * Requirements: k % 1024 == 0, n < 2^30 (TQ_ERR_SHAPE); alignment as above
+ * (TQ_ERR_ALIGN).  Covered: PQ2_0_G128 with k <= 11264 (the decode GEMV's
+ * batch-1 kernel); other valid requests return TQ_ERR_UNSUPPORTED with
+ * nothing enqueued. */
+tq_status tq_head_argmax(const uint8_t *payload, uint64_t payload_bytes, int32_t format,
+                         int64_t n, int64_t k, const void *x, int32_t x_dtype,
+                         const uint16_t *norm_bf16, float eps, const uint16_t *signs_bf16,
+                         float *logits, uint64_t *work, int32_t *token, void *stream);
+
 /* Prefill GEMM: Y[m][n] = sum_g s[n][g] * sum_{j in g} t[n][j] * X[m][j]
  * for m < M rows of rotated activations X (x_dtype TQ_F16 or TQ_BF16,
  * row-major [M][ldx], 16-byte aligned, ldx a multiple of 8) against a

@@ -67,6 +67,11 @@ def activations_bf16_bits(rng, rows, k):
     return f32_to_bf16_bits(activations_f32(rng, rows, k))
 
 
+def norm_weight_bits(rng, k):
+    """bf16 bits of a norm weight near one: 1 + 0.1 * N(0, 1)."""
+    return f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(k)).astype(np.float32))
+
+
 def token_ids(rng, count, n):
     return rng.integers(0, n, size=count, dtype=np.int64).astype(np.int32)
 

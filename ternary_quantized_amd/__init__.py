@@ -40,7 +40,7 @@ EXPORTS = (
     "tq_gemm_rowsplit", "tq_embed_rows_inverse", "tq_decode_rowsplit",
     "tq_rotated_gemv_rowsplit", "tq_blocks_to_planes", "tq_planes_to_blocks",
     "tq_container_parse", "tq_container_object_at", "tq_g64_bytes", "tq_expand_g64",
-    "tq_gemv_g64",
+    "tq_gemv_g64", "tq_head_argmax",
 )
 
 
@@ -94,6 +94,8 @@ def lib():
             "tq_container_object_at": [_vp, _u64, _i64, ctypes.POINTER(ContainerObject)],
             "tq_g64_bytes": [_i64, _i64, ctypes.POINTER(_u64)],
             "tq_expand_g64": [_vp, _u64, _i32, _i64, _i64, _vp, _u64, _vp],
+            "tq_head_argmax": [_vp, _u64, _i32, _i64, _i64, _vp, _i32, _vp, ctypes.c_float, _vp, _vp,
+                               _vp, _vp, _vp],
             "tq_gemv_g64": [_vp, _u64, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _i64, _vp],
         }
         for name, args in sigs.items():
@@ -366,3 +368,21 @@ def gemv_g64(blocks, n, k, xrot, out=None):
                              xrot.data_ptr(), _dtype_code(xrot), batch, xrot.stride(0),
                              out.data_ptr(), out.stride(0), _stream(xrot.device)))
     return out
+
+
+def head_argmax(payload, fmt, n, k, x, norm, eps, signs, work, logits=None, token=None):
+    """Greedy token (int32 device tensor [1]) of the output head step on one
+    hidden row x [k]: RMSNorm(norm, eps), signed transform, head GEMV; the
+    logits go to `logits` [n] fp32 when given.  work: int64 device tensor of
+    two zeroed words (left zero by every call)."""
+    torch = _torch()
+    for t, name in ((payload, "payload"), (x, "x"), (norm, "norm"), (signs, "signs"), (work, "work")):
+        _dev(t, name)
+    if token is None:
+        token = torch.empty(1, dtype=torch.int32, device=x.device)
+    lp = None if logits is None else logits.data_ptr()
+    _check(lib().tq_head_argmax(payload.data_ptr(), payload.numel() * payload.element_size(),
+                                _fmt(fmt), n, k, x.data_ptr(), _dtype_code(x), norm.data_ptr(),
+                                float(eps), _signs_ptr(signs), lp, work.data_ptr(), token.data_ptr(),
+                                _stream(x.device)))
+    return token

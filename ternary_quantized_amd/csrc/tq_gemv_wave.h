@@ -41,6 +41,35 @@ constexpr int CPOL_NT = 2;
 //    [binary16 d][16 code bytes] for 64 weights, with the same code order.
 enum { LAY_PLANES = 0, LAY_G64 = 1 };
 
+// What the kernel does around the product.
+//  MODE_GEMV: x is the rotated activation row.
+//  MODE_ROT:  x is unrotated; the kernel applies the signed transform.
+//  MODE_HEAD: x is the last hidden row; the kernel applies RMSNorm with the
+//             weight g and eps, then the signed transform, and reduces the
+//             products (the logits) to the greedy token.
+enum { MODE_GEMV = 0, MODE_ROT = 1, MODE_HEAD = 2 };
+
+// Extra arguments of MODE_HEAD.  work[0] receives the running maximum of
+// the (logit, index) keys and the low word of work[1] counts finished
+// workgroups; both are zero before a launch and the last workgroup resets
+// them after writing the token.
+struct HeadArgs {
+  const uint16_t *g = nullptr;  // bf16 norm weight [k]
+  float eps = 0.0f;
+  unsigned long long *work = nullptr;
+  int32_t *token = nullptr;
+};
+
+// Order-preserving 64-bit key of (logit v, row i): the float's bits mapped
+// so that unsigned order is numeric order (-0 is taken as +0), above the
+// complement of the index, so that the maximum key is the largest logit
+// with the lowest index.
+__device__ __forceinline__ unsigned long long greedy_key(float v, uint32_t i) {
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)o << 32) | (0xFFFFFFFFu - i);
+}
+
 // ---------------------------------------------------------------------------
 // Batch-1 GEMV, one wave per row.
 //
@@ -128,16 +157,29 @@ __device__ __forceinline__ float rows8_sum(const float (&v)[D], int lane, int &r
 // its next load until rows arrive, which would hold up the staging), unless
 // every wave of the workgroup stages.
 //
-// With FUSED set the kernel also performs the signed transform of its input
+// MODE_ROT: the kernel also performs the signed transform of its input
 // ([tensorsharp] §4.2: a projection input is rotated by H(D.x)/32 per
 // 1024-element block): x is then the unrotated activation row, each staging
 // wave transforms its 1024-element blocks in registers and rounds them to
 // binary16 exactly as the standalone transform with binary16 output does,
 // so one launch covers the whole step with the same result as two.
-template <int LAY, int A, int BQ, int D, int XD, bool FUSED, int WPG>
+//
+// MODE_HEAD: the output head of a decode step ([tensorsharp] §4.4: RMSNorm,
+// signed transform, low-bit head, logits) with the greedy choice fused in
+// (a GEMV that also finds the argmax, as [gguf-explainer] §4.5's drafter
+// kernel does).  The transform is linear, so each staging wave transforms
+// its blocks of x*g and the scalar 1/rms(x) is applied after it, once the
+// staging waves have pooled their sums of squares (in a fixed order).  Each
+// lane that holds a row's logit keeps the largest (logit, index) key, the
+// workgroup takes the maximum over its waves, and one 64-bit atomic maximum
+// per workgroup merges them; the last workgroup to finish writes the token.
+// y (the logits) may be null.
+template <int LAY, int A, int BQ, int D, int XD, int MODE, int WPG>
 __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const void *__restrict__ x,
                                                              const uint16_t *__restrict__ signs,
-                                                             float *__restrict__ y) {
+                                                             float *__restrict__ y, HeadArgs hd) {
+  constexpr bool FUSED = MODE != MODE_GEMV;
+  constexpr bool HEAD = MODE == MODE_HEAD;
   constexpr int NB = 4 * A + BQ;  // 1024-element blocks in a row = 16-weight dwords per lane
   constexpr int NP = A + BQ;      // pieces per lane
   // Activation pairs: dword s of lane l (16 weights, pairs (e, e+8)) is held
@@ -147,6 +189,9 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   __shared__ __attribute__((aligned(16))) u32x4 xq[NB * 128];
   __shared__ float xsum[NP * 64];  // [piece][lane]: sum of the piece's binary16 activations
   __shared__ uint32_t staged;      // staging waves done
+  __shared__ uint32_t sq_posted;   // HEAD: staging waves that posted their sum of squares
+  __shared__ float sq_part[HEAD ? WPG : 1];
+  __shared__ unsigned long long wbest[HEAD ? WPG : 1];
   // the transform's per-wave scratch (staging waves only)
   __shared__ __attribute__((aligned(16))) float wsc[FUSED ? (NB < WPG ? NB : WPG) : 1][1024];
   const int lane = threadIdx.x & 63;
@@ -251,6 +296,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   constexpr int NI = FUSED ? (NB + WPG - 1) / WPG : (NB * 64 + 64 * WPG - 1) / (64 * WPG);
   Raw16<XD> xraw[NI];
   u32x4 sraw[FUSED ? NI : 1][2];
+  u32x4 graw[HEAD ? NI : 1][2];
   auto item = [&](int i) -> int64_t {  // first element of item i of this thread
     if constexpr (FUSED) {
       const int blk = wave + WPG * i < NB ? wave + WPG * i : NB - 1;
@@ -260,7 +306,10 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
       return 16 * (int64_t)(c < NB * 64 ? c : NB * 64 - 1);
     }
   };
-  if (threadIdx.x == 0) staged = 0;
+  if (threadIdx.x == 0) {
+    staged = 0;
+    sq_posted = 0;
+  }
   if (stager) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -269,6 +318,11 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
         const u32x4 *sp = reinterpret_cast<const u32x4 *>(signs + item(i));
         sraw[i][0] = sp[0];
         sraw[i][1] = sp[1];
+      }
+      if constexpr (HEAD) {
+        const u32x4 *gp = reinterpret_cast<const u32x4 *>(hd.g + item(i));
+        graw[i][0] = gp[0];
+        graw[i][1] = gp[1];
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -284,6 +338,38 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
 
   // ---- 3. staging waves: activations -> binary16 pairs in LDS
   if (stager) {
+    // HEAD: the scale of the norm, 1/sqrt(mean(x^2) + eps), folded with the
+    // transform's 1/32; every staging wave posts the sum of squares of its
+    // blocks, waits for the others and adds them in wave order
+    float post = 0.03125f;
+    if constexpr (HEAD) {
+      constexpr uint32_t NSTG = NB < WPG ? NB : WPG;
+      float sq = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        if (wave + WPG * i >= NB) continue;
+        float v[16];
+        convert16<XD>(xraw[i], v);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sq = __builtin_fmaf(v[e], v[e], sq);
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
+      if (lane == 0) sq_part[wave] = sq;
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      if (lane == 0) __hip_atomic_fetch_add(&sq_posted, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      for (int spin = 0; spin < (1 << 22); ++spin) {
+        const uint32_t done = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(&sq_posted, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (done >= NSTG) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      asm volatile("" ::: "memory");
+      float tot = 0.0f;
+#pragma unroll
+      for (uint32_t w = 0; w < NSTG; ++w) tot += sq_part[w];
+      post = 0.03125f / __builtin_sqrtf(tot / (float)(NB * 1024) + hd.eps);
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const bool mine = FUSED ? wave + WPG * i < NB : (int)threadIdx.x + 64 * WPG * i < NB * 64;
@@ -295,6 +381,12 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
         convert16<XD>(xraw[i], v);
         const uint32_t sw[8] = {sraw[i][0][0], sraw[i][0][1], sraw[i][0][2], sraw[i][0][3],
                                 sraw[i][1][0], sraw[i][1][1], sraw[i][1][2], sraw[i][1][3]};
+        if constexpr (HEAD) {
+          const uint32_t gw[8] = {graw[i][0][0], graw[i][0][1], graw[i][0][2], graw[i][0][3],
+                                  graw[i][1][0], graw[i][1][1], graw[i][1][2], graw[i][1][3]};
+#pragma unroll
+          for (int e = 0; e < 16; ++e) v[e] *= bf16_to_f32((uint16_t)(gw[e >> 1] >> (16 * (e & 1))));
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e)
           v[e] = apply_sign(v[e], (uint16_t)(sw[e >> 1] >> (16 * (e & 1))));
@@ -306,10 +398,10 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
         uint16_t *nat = reinterpret_cast<uint16_t *>(sc);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const uint32_t lo = (uint32_t)f32_to_f16(v[4 * g] * 0.03125f) |
-                              ((uint32_t)f32_to_f16(v[4 * g + 1] * 0.03125f) << 16);
-          const uint32_t hi = (uint32_t)f32_to_f16(v[4 * g + 2] * 0.03125f) |
-                              ((uint32_t)f32_to_f16(v[4 * g + 3] * 0.03125f) << 16);
+          const uint32_t lo = (uint32_t)f32_to_f16(v[4 * g] * post) |
+                              ((uint32_t)f32_to_f16(v[4 * g + 1] * post) << 16);
+          const uint32_t hi = (uint32_t)f32_to_f16(v[4 * g + 2] * post) |
+                              ((uint32_t)f32_to_f16(v[4 * g + 3] * post) << 16);
           *reinterpret_cast<u32x2 *>(nat + 256 * g + 4 * lane) = (u32x2){lo, hi};
         }
         const u32x4 *q = reinterpret_cast<const u32x4 *>(nat + 16 * lane);
@@ -401,6 +493,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 5. passes of D rows
+  unsigned long long best = 0;  // HEAD: the lane's largest key (0 is below every logit)
   auto do_pass = [&](int base, auto refill) {
     float part[D];
 #pragma unroll
@@ -438,19 +531,55 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
     }
     int r;
     const float tot = rows8_sum<D>(part, lane, r);
-    if ((lane & 7) == 7 && r < D && base + r < n32) y[base + r] = tot;
+    if ((lane & 7) == 7 && r < D && base + r < n32) {
+      if constexpr (HEAD) {
+        if (y) y[base + r] = tot;
+        const unsigned long long key = greedy_key(tot, (uint32_t)(base + r));
+        best = key > best ? key : best;
+      } else {
+        y[base + r] = tot;
+      }
+    }
   };
   int base = gw32 * D;
   for (; base + D * W32 < n32; base += D * W32) do_pass(base, std::integral_constant<bool, true>{});
   if (base < n32) do_pass(base, std::integral_constant<bool, false>{});
+
+  if constexpr (HEAD) {
+    // the wave's maximum key, then the workgroup's, then one atomic maximum
+    uint32_t hi = (uint32_t)(best >> 32), lo = (uint32_t)best;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint32_t ohi = (uint32_t)__shfl_xor((int)hi, o), olo = (uint32_t)__shfl_xor((int)lo, o);
+      const bool take = ohi > hi || (ohi == hi && olo > lo);
+      hi = take ? ohi : hi;
+      lo = take ? olo : lo;
+    }
+    if (lane == 0) wbest[wave] = ((unsigned long long)hi << 32) | lo;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long m = 0;
+#pragma unroll
+      for (int w = 0; w < WPG; ++w) m = wbest[w] > m ? wbest[w] : m;
+      __hip_atomic_fetch_max(&hd.work[0], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t *done = reinterpret_cast<uint32_t *>(&hd.work[1]);
+      const uint32_t prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev == gridDim.x - 1) {
+        const unsigned long long k = __hip_atomic_load(&hd.work[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        hd.token[0] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+        __hip_atomic_store(&hd.work[0], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
 }
 
-template <int LAY, int A, int BQ, int D, int XD, bool FUSED, int WPG>
+template <int LAY, int A, int BQ, int D, int XD, int MODE, int WPG>
 static hipError_t gemv_wave_launch(const Planes &p, const void *x, const uint16_t *signs, float *y,
-                                   int64_t waves, hipStream_t st) {
+                                   const HeadArgs &hd, int64_t waves, hipStream_t st) {
   const int64_t grid = (waves + WPG - 1) / WPG;
-  hipLaunchKernelGGL((gemv_wave_kernel<LAY, A, BQ, D, XD, FUSED, WPG>), dim3((unsigned)grid),
-                     dim3(64 * WPG), 0, st, p, x, signs, y);
+  hipLaunchKernelGGL((gemv_wave_kernel<LAY, A, BQ, D, XD, MODE, WPG>), dim3((unsigned)grid),
+                     dim3(64 * WPG), 0, st, p, x, signs, y, hd);
   return hipGetLastError();
 }
 
@@ -461,24 +590,24 @@ static hipError_t gemv_wave_launch(const Planes &p, const void *x, const uint16_
 // row their slot already holds.  Workgroup size by register need: three
 // waves per SIMD up to k = 5120 (WPG 12), two up to k = 7168 (WPG 8), one
 // beyond (WPG 4).
-template <int LAY, int A, int BQ, int D, int XD, bool FUSED, int WPG>
+template <int LAY, int A, int BQ, int D, int XD, int MODE, int WPG>
 static const void *gemv_wave_ptr() {
-  return reinterpret_cast<const void *>(gemv_wave_kernel<LAY, A, BQ, D, XD, FUSED, WPG>);
+  return reinterpret_cast<const void *>(gemv_wave_kernel<LAY, A, BQ, D, XD, MODE, WPG>);
 }
 
-template <int LAY, int A, int BQ, int XD, bool FUSED>
+template <int LAY, int A, int BQ, int XD, int MODE>
 static hipError_t gemv_wave_go(const Planes &p, const void *x, const uint16_t *signs, float *y,
-                               hipStream_t st) {
+                               hipStream_t st, const HeadArgs &hd = HeadArgs{}) {
   constexpr int NBK = 4 * A + BQ;
   constexpr int WPG = NBK <= 5 ? 12 : NBK <= 7 ? 8 : 4;
   // ring depths tried: 4, 6, 8; the G64 stream also 5 (its long rows run
   // one wave per SIMD, where 5 rows per wave fill the chip at k = 17408)
   constexpr int ND = LAY == LAY_G64 ? 4 : 3;
   const int depth[4] = {4, 5, 6, 8};
-  const void *kerns[4] = {gemv_wave_ptr<LAY, A, BQ, 4, XD, FUSED, WPG>(), nullptr,
-                          gemv_wave_ptr<LAY, A, BQ, 6, XD, FUSED, WPG>(),
-                          gemv_wave_ptr<LAY, A, BQ, 8, XD, FUSED, WPG>()};
-  if constexpr (LAY == LAY_G64) kerns[1] = gemv_wave_ptr<LAY, A, BQ, 5, XD, FUSED, WPG>();
+  const void *kerns[4] = {gemv_wave_ptr<LAY, A, BQ, 4, XD, MODE, WPG>(), nullptr,
+                          gemv_wave_ptr<LAY, A, BQ, 6, XD, MODE, WPG>(),
+                          gemv_wave_ptr<LAY, A, BQ, 8, XD, MODE, WPG>()};
+  if constexpr (LAY == LAY_G64) kerns[1] = gemv_wave_ptr<LAY, A, BQ, 5, XD, MODE, WPG>();
   const int cus = device_cus();
   int best = -1;
   int64_t best_rows = 0, best_waves = 0;
@@ -502,12 +631,12 @@ static hipError_t gemv_wave_go(const Planes &p, const void *x, const uint16_t *s
   }
   if (best < 0) return hipErrorInvalidConfiguration;
   switch (depth[best]) {
-    case 4: return gemv_wave_launch<LAY, A, BQ, 4, XD, FUSED, WPG>(p, x, signs, y, best_waves, st);
-    case 6: return gemv_wave_launch<LAY, A, BQ, 6, XD, FUSED, WPG>(p, x, signs, y, best_waves, st);
-    case 8: return gemv_wave_launch<LAY, A, BQ, 8, XD, FUSED, WPG>(p, x, signs, y, best_waves, st);
+    case 4: return gemv_wave_launch<LAY, A, BQ, 4, XD, MODE, WPG>(p, x, signs, y, hd, best_waves, st);
+    case 6: return gemv_wave_launch<LAY, A, BQ, 6, XD, MODE, WPG>(p, x, signs, y, hd, best_waves, st);
+    case 8: return gemv_wave_launch<LAY, A, BQ, 8, XD, MODE, WPG>(p, x, signs, y, hd, best_waves, st);
     default:
       if constexpr (LAY == LAY_G64)
-        return gemv_wave_launch<LAY, A, BQ, 5, XD, FUSED, WPG>(p, x, signs, y, best_waves, st);
+        return gemv_wave_launch<LAY, A, BQ, 5, XD, MODE, WPG>(p, x, signs, y, hd, best_waves, st);
       return hipErrorInvalidConfiguration;
   }
 }

@@ -70,6 +70,13 @@ hipError_t launch_expand_g64(int fmt, const uint8_t *base, const uint8_t *high,
 hipError_t launch_gemv_g64(const uint8_t *blocks, int64_t n, int64_t k, const void *x, int x_dtype,
                            float *y, hipStream_t st);
 
+// Output head in one launch (PQ2_0 planes, k = 1024*m with 1 <= m <= 11,
+// batch 1): RMSNorm (bf16 weight g, eps), signed transform, head GEMV into
+// logits (may be null) and the greedy token; work = two zeroed 64-bit words.
+hipError_t launch_head_argmax(const Planes &p, const void *x, int x_dtype, const uint16_t *g,
+                              float eps, const uint16_t *signs, float *logits,
+                              unsigned long long *work, int32_t *token, hipStream_t st);
+
 hipError_t launch_decode(const Planes &p, const int32_t *rows, int64_t count,
                          int8_t *values, uint16_t *scale_bits, int64_t k_pad,
                          hipStream_t stream);
