@@ -315,6 +315,32 @@ def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream):
         del gcps, p2
         torch.cuda.empty_cache()
 
+        # GatedDeltaNet output projection N=5120 K=6144 (48 value heads of 128,
+        # gathered into the grouped head order before the transform), batch 1,
+        # with config 2's value recipe
+        rng = np.random.default_rng(46)
+        n6, k6 = 5120, 6144
+        t6 = synth.trits_sparse(rng, n6, k6)
+        p6 = tq.pack_rowsplit("PQ2_0_G128", t6, synth.scale_bits_lognormal(rng, n6, k6 // 128))
+        del t6
+        s6 = bits_dev(synth.sign_bits(rng, k6), torch.bfloat16)
+        x6 = bits_dev(synth.activations_bf16_bits(rng, 1, k6), torch.bfloat16)
+        nc6 = copies_for(p6.size)
+        cps6 = [to_dev(p6)]
+        cps6 += [cps6[0].clone() for _ in range(nc6 - 1)]
+        y6 = torch.empty((1, n6), dtype=torch.float32, device=x6.device)
+        gmean = event_timed(torch, lambda i: tq.rotated_gemv_rowsplit_grouped(
+            cps6[i % nc6], "PQ2_0_G128", n6, k6, x6, s6, out=y6), 4 * nc6)
+        pmean = event_timed(torch, lambda i: tq.rotated_gemv_rowsplit(
+            cps6[i % nc6], "PQ2_0_G128", n6, k6, x6, s6, out=y6), 4 * nc6)
+        byts = p6.size + 2 * k6 + 2 * k6 + 4 * n6
+        res["gdn_out_proj_grouped_step"] = {"n": n6, "k": k6, "mean_launch_us": round(gmean * 1e6, 3),
+                                            "gbs": round(byts / gmean / 1e9, 1),
+                                            "frac_hbm": round(byts / gmean / 1e9 / HBM_PEAK_GBS, 4),
+                                            "same_step_without_gather_us": round(pmean * 1e6, 3)}
+        del cps6
+        torch.cuda.empty_cache()
+
         # config 4: vocabulary head N=248320 K=5120 batch 1 + 64 embedding rows
         c4 = synth.make_config(4)
         p4 = tq.pack_rowsplit(c4["fmt"], c4["trits"], c4["scale_bits"])

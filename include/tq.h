@@ -245,6 +245,25 @@ tq_status tq_hadamard_signed(const void *x, int32_t x_dtype, int64_t rows,
                              void *y, int32_t y_dtype, int64_t ldy,
                              void *stream);
 
+/* The signed transform of a row held in the tiled head order, taken in the
+ * grouped head order first ([ninfer-skill] §5 perm48 / perm_row; [tensorsharp]
+ * §4.2: with grouped GatedDeltaNet metadata the input of the projection
+ * after the GatedDeltaNet is reordered into the publisher's head order
+ * before its transform):
+ *   r[j] = x[src(j)],  src(h*head_dim + i) = ((h % tiles)*groups + h/tiles)*head_dim + i
+ *   y_b = H (d_b . r_b) / 32  per 1024-element block b (as tq_hadamard_signed
+ *   with inverse 0).
+ * The model's value heads: tiles 3, groups 16, head_dim 128 (k = 6144; target
+ * head g*3+t comes from source head t*16+g).  Reading: r[j] = x[src(j)], the
+ * page's "source row" of row j.
+ * Requirements: as tq_hadamard_signed; tiles, groups >= 1, head_dim a
+ * multiple of 16 and tiles*groups*head_dim == k (TQ_ERR_SHAPE); x and y must
+ * not overlap (TQ_ERR_ARG). */
+tq_status tq_hadamard_signed_grouped(const void *x, int32_t x_dtype, int64_t rows, int64_t k,
+                                     int64_t ldx, int32_t tiles, int32_t groups,
+                                     int32_t head_dim, const uint16_t *signs_bf16, void *y,
+                                     int32_t y_dtype, int64_t ldy, void *stream);
+
 /* Decode GEMV: y[b][n] = sum_g s[n][g] * sum_{j in g} t[n][j] * xrot[b][j]
  * for b < batch, n < N, over the row-split payload (`payload`, exactly
  * payload_bytes bytes, 256-byte aligned).  xrot: already-rotated
@@ -301,6 +320,17 @@ tq_status tq_head_argmax(const uint8_t *payload, uint64_t payload_bytes, int32_t
                          int64_t n, int64_t k, const void *x, int32_t x_dtype,
                          const uint16_t *norm_bf16, float eps, const uint16_t *signs_bf16,
                          float *logits, uint64_t *work, int32_t *token, void *stream);
+
+/* tq_rotated_gemv_rowsplit with the grouped head order: the signed
+ * transform input is x gathered as for tq_hadamard_signed_grouped, i.e.
+ * exactly tq_hadamard_signed_grouped (y_dtype F16) then tq_gemv_rowsplit, in
+ * one launch.  Requirements and coverage as for both. */
+tq_status tq_rotated_gemv_rowsplit_grouped(const uint8_t *payload, uint64_t payload_bytes,
+                                           int32_t format, int64_t n, int64_t k, const void *x,
+                                           int32_t x_dtype, int64_t batch, int64_t ldx,
+                                           int32_t tiles, int32_t groups, int32_t head_dim,
+                                           const uint16_t *signs_bf16, float *y, int64_t ldy,
+                                           void *stream);
 
 /* Prefill GEMM: Y[m][n] = sum_g s[n][g] * sum_{j in g} t[n][j] * X[m][j]
  * for m < M rows of rotated activations X (x_dtype TQ_F16 or TQ_BF16,

@@ -40,7 +40,8 @@ EXPORTS = (
     "tq_gemm_rowsplit", "tq_embed_rows_inverse", "tq_decode_rowsplit",
     "tq_rotated_gemv_rowsplit", "tq_blocks_to_planes", "tq_planes_to_blocks",
     "tq_container_parse", "tq_container_object_at", "tq_g64_bytes", "tq_expand_g64",
-    "tq_gemv_g64", "tq_head_argmax",
+    "tq_gemv_g64", "tq_head_argmax", "tq_hadamard_signed_grouped",
+    "tq_rotated_gemv_rowsplit_grouped",
 )
 
 
@@ -96,6 +97,10 @@ def lib():
             "tq_expand_g64": [_vp, _u64, _i32, _i64, _i64, _vp, _u64, _vp],
             "tq_head_argmax": [_vp, _u64, _i32, _i64, _i64, _vp, _i32, _vp, ctypes.c_float, _vp, _vp,
                                _vp, _vp, _vp],
+            "tq_hadamard_signed_grouped": [_vp, _i32, _i64, _i64, _i64, _i32, _i32, _i32, _vp, _vp, _i32,
+                                           _i64, _vp],
+            "tq_rotated_gemv_rowsplit_grouped": [_vp, _u64, _i32, _i64, _i64, _vp, _i32, _i64, _i64,
+                                                 _i32, _i32, _i32, _vp, _vp, _i64, _vp],
             "tq_gemv_g64": [_vp, _u64, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _i64, _vp],
         }
         for name, args in sigs.items():
@@ -386,3 +391,45 @@ def head_argmax(payload, fmt, n, k, x, norm, eps, signs, work, logits=None, toke
                                 float(eps), _signs_ptr(signs), lp, work.data_ptr(), token.data_ptr(),
                                 _stream(x.device)))
     return token
+
+
+# grouped value-head order of the model: 3 x 16 heads of 128
+GDN_TILES, GDN_GROUPS, GDN_HEAD_DIM = 3, 16, 128
+
+
+def hadamard_signed_grouped(x, signs, tiles=GDN_TILES, groups=GDN_GROUPS, head_dim=GDN_HEAD_DIM,
+                            out_dtype=None, out=None):
+    """Forward signed transform of rows x [rows, k] taken in the grouped head order."""
+    torch = _torch()
+    _dev(x, "x")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D tensor with unit column stride")
+    rows, k = x.shape
+    if out is None:
+        out = torch.empty((rows, k), dtype=out_dtype or x.dtype, device=x.device)
+    _check(lib().tq_hadamard_signed_grouped(x.data_ptr(), _dtype_code(x), rows, k,
+                                            x.stride(0) if rows else k, tiles, groups, head_dim,
+                                            _signs_ptr(signs), out.data_ptr(), _dtype_code(out),
+                                            out.stride(0) if rows else k, _stream(x.device)))
+    return out
+
+
+def rotated_gemv_rowsplit_grouped(payload, fmt, n, k, x, signs, tiles=GDN_TILES, groups=GDN_GROUPS,
+                                  head_dim=GDN_HEAD_DIM, out=None):
+    """y [batch, n] fp32 = decode-GEMV of the signed transform of x [batch, k]
+    taken in the grouped head order, in one launch."""
+    torch = _torch()
+    _dev(payload, "payload")
+    _dev(x, "x")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    batch = x.shape[0]
+    if out is None:
+        out = torch.empty((batch, n), dtype=torch.float32, device=x.device)
+    _check(lib().tq_rotated_gemv_rowsplit_grouped(
+        payload.data_ptr(), payload.numel() * payload.element_size(), _fmt(fmt), n, k, x.data_ptr(),
+        _dtype_code(x), batch, x.stride(0), tiles, groups, head_dim, _signs_ptr(signs),
+        out.data_ptr(), out.stride(0), _stream(x.device)))
+    return out

@@ -513,10 +513,10 @@ __global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restri
 
 template <int A, int BQ, bool FUSED>
 static hipError_t gemv_wave_dt(const Planes &p, const void *x, int xd, const uint16_t *signs,
-                               float *y, hipStream_t st) {
-  if (xd == DT_F32) return gemv_wave_go<LAY_PLANES, A, BQ, DT_F32, FUSED>(p, x, signs, y, st);
-  if (xd == DT_BF16) return gemv_wave_go<LAY_PLANES, A, BQ, DT_BF16, FUSED>(p, x, signs, y, st);
-  return gemv_wave_go<LAY_PLANES, A, BQ, DT_F16, FUSED>(p, x, signs, y, st);
+                               float *y, hipStream_t st, const StepArgs &sa) {
+  if (xd == DT_F32) return gemv_wave_go<LAY_PLANES, A, BQ, DT_F32, FUSED>(p, x, signs, y, st, sa);
+  if (xd == DT_BF16) return gemv_wave_go<LAY_PLANES, A, BQ, DT_BF16, FUSED>(p, x, signs, y, st, sa);
+  return gemv_wave_go<LAY_PLANES, A, BQ, DT_F16, FUSED>(p, x, signs, y, st, sa);
 }
 
 // k = 1024*m with m <= 11: pieces A = m/4 kilobytes + BQ = m%4 blocks.
@@ -527,19 +527,19 @@ static bool gemv_wave_fits(const Planes &p) {
 
 template <bool FUSED>
 static hipError_t gemv_wave(const Planes &p, const void *x, int xd, const uint16_t *signs, float *y,
-                            hipStream_t st) {
+                            hipStream_t st, const StepArgs &sa = StepArgs{}) {
   switch (p.k / 1024) {
-    case 1: return gemv_wave_dt<0, 1, FUSED>(p, x, xd, signs, y, st);
-    case 2: return gemv_wave_dt<0, 2, FUSED>(p, x, xd, signs, y, st);
-    case 3: return gemv_wave_dt<0, 3, FUSED>(p, x, xd, signs, y, st);
-    case 4: return gemv_wave_dt<1, 0, FUSED>(p, x, xd, signs, y, st);
-    case 5: return gemv_wave_dt<1, 1, FUSED>(p, x, xd, signs, y, st);
-    case 6: return gemv_wave_dt<1, 2, FUSED>(p, x, xd, signs, y, st);
-    case 7: return gemv_wave_dt<1, 3, FUSED>(p, x, xd, signs, y, st);
-    case 8: return gemv_wave_dt<2, 0, FUSED>(p, x, xd, signs, y, st);
-    case 9: return gemv_wave_dt<2, 1, FUSED>(p, x, xd, signs, y, st);
-    case 10: return gemv_wave_dt<2, 2, FUSED>(p, x, xd, signs, y, st);
-    default: return gemv_wave_dt<2, 3, FUSED>(p, x, xd, signs, y, st);
+    case 1: return gemv_wave_dt<0, 1, FUSED>(p, x, xd, signs, y, st, sa);
+    case 2: return gemv_wave_dt<0, 2, FUSED>(p, x, xd, signs, y, st, sa);
+    case 3: return gemv_wave_dt<0, 3, FUSED>(p, x, xd, signs, y, st, sa);
+    case 4: return gemv_wave_dt<1, 0, FUSED>(p, x, xd, signs, y, st, sa);
+    case 5: return gemv_wave_dt<1, 1, FUSED>(p, x, xd, signs, y, st, sa);
+    case 6: return gemv_wave_dt<1, 2, FUSED>(p, x, xd, signs, y, st, sa);
+    case 7: return gemv_wave_dt<1, 3, FUSED>(p, x, xd, signs, y, st, sa);
+    case 8: return gemv_wave_dt<2, 0, FUSED>(p, x, xd, signs, y, st, sa);
+    case 9: return gemv_wave_dt<2, 1, FUSED>(p, x, xd, signs, y, st, sa);
+    case 10: return gemv_wave_dt<2, 2, FUSED>(p, x, xd, signs, y, st, sa);
+    default: return gemv_wave_dt<2, 3, FUSED>(p, x, xd, signs, y, st, sa);
   }
 }
 
@@ -888,8 +888,12 @@ bool rotated_gemv_fused(const Planes &p, int64_t batch) {
 }
 
 hipError_t launch_rotated_gemv(const Planes &p, const void *x, int xd, const uint16_t *signs,
-                               float *y, hipStream_t st) {
-  return gemv_wave<true>(p, x, xd, signs, y, st);
+                               float *y, hipStream_t st, int tiles, int groups, int head_dim) {
+  StepArgs sa;
+  sa.tiles = tiles;
+  sa.groups = groups;
+  sa.head_dim = head_dim;
+  return gemv_wave<true>(p, x, xd, signs, y, st, sa);
 }
 
 }  // namespace tq

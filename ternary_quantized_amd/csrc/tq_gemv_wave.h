@@ -49,16 +49,30 @@ enum { LAY_PLANES = 0, LAY_G64 = 1 };
 //             products (the logits) to the greedy token.
 enum { MODE_GEMV = 0, MODE_ROT = 1, MODE_HEAD = 2 };
 
-// Extra arguments of MODE_HEAD.  work[0] receives the running maximum of
-// the (logit, index) keys and the low word of work[1] counts finished
-// workgroups; both are zero before a launch and the last workgroup resets
-// them after writing the token.
-struct HeadArgs {
+// Extra arguments of the fused modes.
+//  MODE_HEAD: work[0] receives the running maximum of the (logit, index)
+//    keys and the low word of work[1] counts finished workgroups; both are
+//    zero before a launch and the last workgroup resets them after writing
+//    the token.
+//  MODE_ROT with tiles > 0: the transform input is x in the grouped head
+//    order, element j taken from x[head_src(j)] (head_src below).
+struct StepArgs {
   const uint16_t *g = nullptr;  // bf16 norm weight [k]
   float eps = 0.0f;
   unsigned long long *work = nullptr;
   int32_t *token = nullptr;
+  int tiles = 0, groups = 0, head_dim = 0;
 };
+
+// Source position of transform-input element j in the grouped head order
+// ([ninfer-skill] §5 perm_row, generalised): heads of head_dim elements, the
+// target head h taken from source head (h % tiles) * groups + h / tiles.
+// head_dim is a multiple of 16, so 16 consecutive elements from a multiple
+// of 16 stay inside one head and move together.
+__device__ __forceinline__ int head_src(int j, int tiles, int groups, int head_dim) {
+  const int h = j / head_dim;
+  return ((h % tiles) * groups + h / tiles) * head_dim + (j - h * head_dim);
+}
 
 // Order-preserving 64-bit key of (logit v, row i): the float's bits mapped
 // so that unsigned order is numeric order (-0 is taken as +0), above the
@@ -177,7 +191,7 @@ __device__ __forceinline__ float rows8_sum(const float (&v)[D], int lane, int &r
 template <int LAY, int A, int BQ, int D, int XD, int MODE, int WPG>
 __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const void *__restrict__ x,
                                                              const uint16_t *__restrict__ signs,
-                                                             float *__restrict__ y, HeadArgs hd) {
+                                                             float *__restrict__ y, StepArgs hd) {
   constexpr bool FUSED = MODE != MODE_GEMV;
   constexpr bool HEAD = MODE == MODE_HEAD;
   constexpr int NB = 4 * A + BQ;  // 1024-element blocks in a row = 16-weight dwords per lane
@@ -313,7 +327,13 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   if (stager) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      load16_raw<XD>(x, item(i), xraw[i]);
+      if constexpr (MODE == MODE_ROT) {
+        const int64_t e = item(i);
+        load16_raw<XD>(x, hd.tiles ? (int64_t)head_src((int)e, hd.tiles, hd.groups, hd.head_dim) : e,
+                       xraw[i]);
+      } else {
+        load16_raw<XD>(x, item(i), xraw[i]);
+      }
       if constexpr (FUSED) {
         const u32x4 *sp = reinterpret_cast<const u32x4 *>(signs + item(i));
         sraw[i][0] = sp[0];
@@ -576,7 +596,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
 
 template <int LAY, int A, int BQ, int D, int XD, int MODE, int WPG>
 static hipError_t gemv_wave_launch(const Planes &p, const void *x, const uint16_t *signs, float *y,
-                                   const HeadArgs &hd, int64_t waves, hipStream_t st) {
+                                   const StepArgs &hd, int64_t waves, hipStream_t st) {
   const int64_t grid = (waves + WPG - 1) / WPG;
   hipLaunchKernelGGL((gemv_wave_kernel<LAY, A, BQ, D, XD, MODE, WPG>), dim3((unsigned)grid),
                      dim3(64 * WPG), 0, st, p, x, signs, y, hd);
@@ -597,7 +617,7 @@ static const void *gemv_wave_ptr() {
 
 template <int LAY, int A, int BQ, int XD, int MODE>
 static hipError_t gemv_wave_go(const Planes &p, const void *x, const uint16_t *signs, float *y,
-                               hipStream_t st, const HeadArgs &hd = HeadArgs{}) {
+                               hipStream_t st, const StepArgs &hd = StepArgs{}) {
   constexpr int NBK = 4 * A + BQ;
   constexpr int WPG = NBK <= 5 ? 12 : NBK <= 7 ? 8 : 4;
   // ring depths tried: 4, 6, 8; the G64 stream also 5 (its long rows run

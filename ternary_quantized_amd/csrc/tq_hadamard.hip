@@ -18,10 +18,17 @@
 
 namespace tq {
 
+// Forward transforms may read their input in the grouped head order
+// ([ninfer-skill] §5 perm_row; [tensorsharp] §4.2: the GatedDeltaNet output
+// is reordered into the publisher's head order before its transform): with
+// tiles > 0, element j of the transform input is x[src(j)], j = h*head_dim +
+// i taken from head (h % tiles)*groups + h/tiles.  head_dim is a multiple of
+// 16, so a lane's 16 elements stay one contiguous load.
 template <int XD, int YD>
 __global__ __launch_bounds__(256) void hadamard_kernel(
     const void *x, int64_t ldx, int64_t rows, int64_t nblocks,
-    const uint16_t *__restrict__ signs, int inverse, void *y, int64_t ldy) {
+    const uint16_t *__restrict__ signs, int inverse, void *y, int64_t ldy,
+    int tiles, int groups, int head_dim) {
   __shared__ __attribute__((aligned(16))) float scratch[4][1024];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -31,8 +38,13 @@ __global__ __launch_bounds__(256) void hadamard_kernel(
   const int64_t blk = (item % nblocks) * 1024;
   const int64_t col = blk + 16 * lane;
 
+  int64_t src = col;
+  if (tiles > 0) {
+    const int h = (int)col / head_dim;
+    src = (int64_t)((h % tiles) * groups + h / tiles) * head_dim + (col - (int64_t)h * head_dim);
+  }
   float v[16];
-  load16<XD>(x, row * ldx + col, v);
+  load16<XD>(x, row * ldx + src, v);
   if (!inverse) {
     const uint4 *sp = reinterpret_cast<const uint4 *>(signs + col);
     uint4 a = sp[0], b = sp[1];
@@ -62,22 +74,22 @@ __global__ __launch_bounds__(256) void hadamard_kernel(
 template <int XD>
 static hipError_t launch_h2(const void *x, int64_t rows, int64_t k, int64_t ldx,
                             const uint16_t *signs, int inverse, void *y, int yd,
-                            int64_t ldy, hipStream_t st) {
+                            int64_t ldy, hipStream_t st, int tiles, int groups, int head_dim) {
   const int64_t nblocks = k / 1024;
   const int64_t items = rows * nblocks;
   dim3 grid((unsigned)((items + 3) / 4)), block(256);
   switch (yd) {
     case DT_F32:
       hipLaunchKernelGGL((hadamard_kernel<XD, DT_F32>), grid, block, 0, st, x, ldx,
-                         rows, nblocks, signs, inverse, y, ldy);
+                         rows, nblocks, signs, inverse, y, ldy, tiles, groups, head_dim);
       break;
     case DT_BF16:
       hipLaunchKernelGGL((hadamard_kernel<XD, DT_BF16>), grid, block, 0, st, x, ldx,
-                         rows, nblocks, signs, inverse, y, ldy);
+                         rows, nblocks, signs, inverse, y, ldy, tiles, groups, head_dim);
       break;
     default:
       hipLaunchKernelGGL((hadamard_kernel<XD, DT_F16>), grid, block, 0, st, x, ldx,
-                         rows, nblocks, signs, inverse, y, ldy);
+                         rows, nblocks, signs, inverse, y, ldy, tiles, groups, head_dim);
       break;
   }
   return hipGetLastError();
@@ -85,11 +97,15 @@ static hipError_t launch_h2(const void *x, int64_t rows, int64_t k, int64_t ldx,
 
 hipError_t launch_hadamard(const void *x, int xd, int64_t rows, int64_t k,
                            int64_t ldx, const uint16_t *signs, int inverse,
-                           void *y, int yd, int64_t ldy, hipStream_t st) {
+                           void *y, int yd, int64_t ldy, hipStream_t st, int tiles,
+                           int groups, int head_dim) {
   switch (xd) {
-    case DT_F32: return launch_h2<DT_F32>(x, rows, k, ldx, signs, inverse, y, yd, ldy, st);
-    case DT_BF16: return launch_h2<DT_BF16>(x, rows, k, ldx, signs, inverse, y, yd, ldy, st);
-    default: return launch_h2<DT_F16>(x, rows, k, ldx, signs, inverse, y, yd, ldy, st);
+    case DT_F32:
+      return launch_h2<DT_F32>(x, rows, k, ldx, signs, inverse, y, yd, ldy, st, tiles, groups, head_dim);
+    case DT_BF16:
+      return launch_h2<DT_BF16>(x, rows, k, ldx, signs, inverse, y, yd, ldy, st, tiles, groups, head_dim);
+    default:
+      return launch_h2<DT_F16>(x, rows, k, ldx, signs, inverse, y, yd, ldy, st, tiles, groups, head_dim);
   }
 }
 

@@ -14,7 +14,7 @@ namespace {
 
 template <int A, int BQ>
 hipError_t head_dt(const Planes &p, const void *x, int xd, const uint16_t *signs, float *logits,
-                   const HeadArgs &hd, hipStream_t st) {
+                   const StepArgs &hd, hipStream_t st) {
   if (xd == DT_F32) return gemv_wave_go<LAY_PLANES, A, BQ, DT_F32, MODE_HEAD>(p, x, signs, logits, st, hd);
   if (xd == DT_BF16) return gemv_wave_go<LAY_PLANES, A, BQ, DT_BF16, MODE_HEAD>(p, x, signs, logits, st, hd);
   return gemv_wave_go<LAY_PLANES, A, BQ, DT_F16, MODE_HEAD>(p, x, signs, logits, st, hd);
@@ -25,7 +25,7 @@ hipError_t head_dt(const Planes &p, const void *x, int xd, const uint16_t *signs
 hipError_t launch_head_argmax(const Planes &p, const void *x, int x_dtype, const uint16_t *g,
                               float eps, const uint16_t *signs, float *logits,
                               unsigned long long *work, int32_t *token, hipStream_t st) {
-  HeadArgs hd;
+  StepArgs hd;
   hd.g = g;
   hd.eps = eps;
   hd.work = work;

@@ -127,6 +127,20 @@ tq_status check_device_payload(const uint8_t *payload, uint64_t payload_bytes,
   return TQ_OK;
 }
 
+// Grouped head order ([ninfer-skill] §5): tiles x groups heads of head_dim
+// elements covering the row exactly.
+tq_status check_head_order(int64_t k, int32_t tiles, int32_t groups, int32_t head_dim) {
+  if (tiles < 1 || groups < 1 || head_dim < 16 || head_dim % 16)
+    return fail(TQ_ERR_SHAPE, "head order needs tiles, groups >= 1 and head_dim a positive "
+                "multiple of 16 (got %d, %d, %d)", (int)tiles, (int)groups, (int)head_dim);
+  if ((int64_t)tiles * groups * head_dim != k)
+    return fail(TQ_ERR_SHAPE, "tiles * groups * head_dim = %lld must equal k = %lld",
+                (long long)tiles * groups * head_dim, (long long)k);
+  return TQ_OK;
+}
+
+size_t dtype_size(int32_t d) { return d == TQ_F32 ? 4 : 2; }
+
 tq_status check_signs(const uint16_t *signs) {
   if (!signs) return fail(TQ_ERR_ARG, "signs_bf16 is NULL");
   if (!aligned(signs, 16))
@@ -275,6 +289,34 @@ tq_status tq_hadamard_signed(const void *x, int32_t x_dtype, int64_t rows,
                        "tq_hadamard_signed");
 }
 
+tq_status tq_hadamard_signed_grouped(const void *x, int32_t x_dtype, int64_t rows, int64_t k,
+                                     int64_t ldx, int32_t tiles, int32_t groups,
+                                     int32_t head_dim, const uint16_t *signs, void *y,
+                                     int32_t y_dtype, int64_t ldy, void *stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(y_dtype))
+    return fail(TQ_ERR_ARG, "x_dtype/y_dtype must be TQ_F32, TQ_BF16 or TQ_F16");
+  if (rows < 0) return fail(TQ_ERR_SHAPE, "rows must be >= 0");
+  if (k < 1 || k % 1024)
+    return fail(TQ_ERR_SHAPE, "k=%lld: the transform needs a positive multiple of the "
+                "1024-element Hadamard block", (long long)k);
+  tq_status st = check_head_order(k, tiles, groups, head_dim);
+  if (st != TQ_OK) return st;
+  if (ldx < k || ldy < k) return fail(TQ_ERR_ARG, "ldx and ldy must be >= k");
+  if ((st = check_signs(signs)) != TQ_OK) return st;
+  if (rows == 0) return TQ_OK;
+  if (!x || !y) return fail(TQ_ERR_ARG, "x and y must be non-NULL");
+  if (!aligned(x, 16) || !aligned(y, 16) || ldx % 8 || ldy % 8)
+    return fail(TQ_ERR_ALIGN, "x and y must be 16-byte aligned with ldx, ldy multiples of 8");
+  const char *xb = static_cast<const char *>(x), *yb = static_cast<const char *>(y);
+  const int64_t xe = ((rows - 1) * ldx + k) * (int64_t)dtype_size(x_dtype);
+  const int64_t ye = ((rows - 1) * ldy + k) * (int64_t)dtype_size(y_dtype);
+  if (xb < yb + ye && yb < xb + xe)
+    return fail(TQ_ERR_ARG, "x and y overlap (the head gather cannot run in place)");
+  return device_status(tq::launch_hadamard(x, x_dtype, rows, k, ldx, signs, 0, y, y_dtype, ldy,
+                                           (hipStream_t)stream, tiles, groups, head_dim),
+                       "tq_hadamard_signed_grouped");
+}
+
 tq_status tq_gemv_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
                            int32_t format, int64_t n, int64_t k, const void *xrot,
                            int32_t x_dtype, int64_t batch, int64_t ldx, float *y,
@@ -328,6 +370,37 @@ tq_status tq_rotated_gemv_rowsplit(const uint8_t *payload, uint64_t payload_byte
   return device_status(tq::launch_rotated_gemv(p, x, x_dtype, signs_bf16, y,
                                                (hipStream_t)stream),
                        "tq_rotated_gemv_rowsplit");
+}
+
+tq_status tq_rotated_gemv_rowsplit_grouped(const uint8_t *payload, uint64_t payload_bytes,
+                                           int32_t format, int64_t n, int64_t k, const void *x,
+                                           int32_t x_dtype, int64_t batch, int64_t ldx,
+                                           int32_t tiles, int32_t groups, int32_t head_dim,
+                                           const uint16_t *signs_bf16, float *y, int64_t ldy,
+                                           void *stream) {
+  tq_geometry g;
+  tq::Planes p;
+  tq_status st = check_device_payload(payload, payload_bytes, format, n, k, &g, &p);
+  if (st != TQ_OK) return st;
+  if (k % 1024)
+    return fail(TQ_ERR_SHAPE, "k=%lld: the transform needs a multiple of the 1024-element block",
+                (long long)k);
+  if ((st = check_head_order(k, tiles, groups, head_dim)) != TQ_OK) return st;
+  if (batch < 1 || batch > 8) return fail(TQ_ERR_SHAPE, "batch=%lld must be in 1..8", (long long)batch);
+  if (!dtype_ok(x_dtype)) return fail(TQ_ERR_ARG, "x_dtype must be TQ_F32, TQ_BF16 or TQ_F16");
+  if (!x || !y) return fail(TQ_ERR_ARG, "x and y must be non-NULL");
+  if ((st = check_signs(signs_bf16)) != TQ_OK) return st;
+  if (ldx < k || ldy < n) return fail(TQ_ERR_ARG, "ldx must be >= k and ldy >= n");
+  if (!aligned(x, 16) || ldx % 8)
+    return fail(TQ_ERR_ALIGN, "x must be 16-byte aligned with ldx a multiple of 8");
+  if (!aligned(y, 4)) return fail(TQ_ERR_ALIGN, "y must be 4-byte aligned");
+  if (!tq::rotated_gemv_fused(p, batch))
+    return fail(TQ_ERR_UNSUPPORTED,
+                "the fused transform + GEMV covers PQ2_0_G128, batch 1, k <= 11264; "
+                "use tq_hadamard_signed_grouped then tq_gemv_rowsplit");
+  return device_status(tq::launch_rotated_gemv(p, x, x_dtype, signs_bf16, y, (hipStream_t)stream,
+                                               tiles, groups, head_dim),
+                       "tq_rotated_gemv_rowsplit_grouped");
 }
 
 tq_status tq_gemm_rowsplit(const uint8_t *payload, uint64_t payload_bytes,

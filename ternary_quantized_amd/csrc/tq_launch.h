@@ -22,7 +22,8 @@ struct Planes {
 hipError_t launch_hadamard(const void *x, int x_dtype, int64_t rows, int64_t k,
                            int64_t ldx, const uint16_t *signs, int inverse,
                            void *y, int y_dtype, int64_t ldy,
-                           hipStream_t stream);
+                           hipStream_t stream, int tiles = 0, int groups = 0,
+                           int head_dim = 0);
 
 hipError_t launch_gemv(const Planes &p, const void *x, int x_dtype,
                        int64_t batch, int64_t ldx, float *y, int64_t ldy,
@@ -41,10 +42,12 @@ hipError_t launch_gemv_ptq1(const Planes &p, const void *x, int x_dtype, int64_t
                             int64_t ldx, float *y, int64_t ldy, hipStream_t stream);
 
 // Signed transform fused into the GEMV (one launch): supported shapes, and
-// the launch itself (x unrotated, signs bf16 +-1).
+// the launch itself (x unrotated, signs bf16 +-1; tiles > 0 gathers x into
+// the grouped head order of tiles x groups heads of head_dim first).
 bool rotated_gemv_fused(const Planes &p, int64_t batch);
 hipError_t launch_rotated_gemv(const Planes &p, const void *x, int x_dtype,
-                               const uint16_t *signs, float *y, hipStream_t st);
+                               const uint16_t *signs, float *y, hipStream_t st,
+                               int tiles = 0, int groups = 0, int head_dim = 0);
 
 // compute units of the current device (cached per device)
 int device_cus();
