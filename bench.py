@@ -224,6 +224,8 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(c2, step_bytes)
+        if not args.no_secondary:
+            cpu["other_rows"] = oracle_rows(synth)
 
     out = {
         "metric": "ternary GEMV achieved HBM GB/s (% of peak) + prefill GEMM TFLOP/s, 1xMI355X",
@@ -443,6 +445,86 @@ def cpu_baseline(c2, step_bytes):
             "sample": "%d full config-2 steps (float64 transform + projection of all 17408 rows)"
                       % reps,
             "seconds_per_step": round(elapsed / reps, 3)}
+
+
+def _timed(fn, min_seconds=1.0, max_reps=50):
+    """(calls, seconds) of repeated fn() until min_seconds have passed."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= max_reps:
+            return reps, el
+
+
+def oracle_rows(synth):
+    """The oracle (test infrastructure) on bounded samples of the other
+    workloads, one thread, in the unit of the matching secondary figure:
+    payload-plus-activation GB/s for the projections, bytes moved for the
+    expansion and the transcoder, TFLOP/s for the GEMM, microseconds for the
+    64 embedding rows."""
+    from threadpoolctl import threadpool_limits
+    from oracle import codec, gdn, head as Hd, projection as P, q2g64, transform as T
+    res = {}
+    rows = 256
+    with threadpool_limits(1):
+        # PTQ1_0 down projection (config 3 recipe), batch 1
+        c = synth.make_config(3, n=rows)
+        pay = codec.pack_rowsplit(c["fmt"], c["trits"], c["scale_bits"])
+        x = T.forward(T.bf16_bits_to_f64(c["x"][:1]), T.bf16_bits_to_f64(c["sign_bits"]))
+        reps, el = _timed(lambda: P.project_payload(c["fmt"], rows, c["k"], pay, x))
+        res["cfg3_ptq1_down_b1"] = {"gbs": round(pay.size * reps / el / 1e9, 5),
+                                    "sample": "%d rows x %d" % (rows, c["k"])}
+        # G64 expansion and the GEMV over the expanded stream
+        reps, el = _timed(lambda: q2g64.expand(c["fmt"], rows, c["k"], pay))
+        gb = q2g64.expanded_bytes(rows, c["k"])
+        res["cfg3_expand_g64"] = {"gbs": round((pay.size + gb) * reps / el / 1e9, 5),
+                                  "sample": "%d rows x %d" % (rows, c["k"])}
+        st = q2g64.expand(c["fmt"], rows, c["k"], pay)
+        reps, el = _timed(lambda: q2g64.project(st, rows, c["k"], x))
+        res["cfg3_expanded_g64_b1"] = {"gbs": round(gb * reps / el / 1e9, 5),
+                                       "sample": "%d rows x %d" % (rows, c["k"])}
+        # the head step (config 4 recipe): norm, transform, projection, greedy
+        c = synth.make_config(4, n=4 * rows)
+        pay = codec.pack_rowsplit(c["fmt"], c["trits"], c["scale_bits"])
+        g = T.bf16_bits_to_f64(synth.norm_weight_bits(np.random.default_rng(44), c["k"]))
+        d = T.bf16_bits_to_f64(c["sign_bits"])
+        xh = T.bf16_bits_to_f64(c["x"])
+        reps, el = _timed(lambda: Hd.greedy(Hd.head(c["fmt"], 4 * rows, c["k"], pay, xh, g, 1e-6, d)[0]))
+        res["cfg4_head_greedy"] = {"gbs": round(pay.size * reps / el / 1e9, 5),
+                                   "sample": "%d rows x %d" % (4 * rows, c["k"])}
+        # block stream -> planes (head recipe)
+        blk = codec.planes_to_blocks(c["fmt"], 4 * rows, c["k"], pay)
+        reps, el = _timed(lambda: codec.blocks_to_planes(c["fmt"], 4 * rows, c["k"], blk))
+        res["transcode_blocks_to_planes"] = {"gbs": round((blk.size + pay.size) * reps / el / 1e9, 5),
+                                             "sample": "%d rows x %d" % (4 * rows, c["k"])}
+        # 64 embedding rows with the inverse transform
+        cf = synth.make_config(4, n=4096)
+        payf = codec.pack_rowsplit(cf["fmt"], cf["trits"], cf["scale_bits"])
+        ids = cf["ids"] % 4096
+        reps, el = _timed(lambda: P.embed_rows_inverse(cf["fmt"], 4096, cf["k"], payf, ids,
+                                                       T.bf16_bits_to_f64(cf["sign_bits"])))
+        res["cfg4_embed_64_rows"] = {"us": round(el / reps * 1e6, 1), "sample": "64 rows of a 4096-row table"}
+        # GatedDeltaNet output projection with the grouped head order
+        rng = np.random.default_rng(46)
+        k6 = 6144
+        t6 = synth.trits_sparse(rng, rows, k6)
+        pay6 = codec.pack_rowsplit("PQ2_0_G128", t6, synth.scale_bits_lognormal(rng, rows, k6 // 128))
+        d6 = T.bf16_bits_to_f64(synth.sign_bits(rng, k6))
+        x6 = T.bf16_bits_to_f64(synth.activations_bf16_bits(rng, 1, k6))
+        reps, el = _timed(lambda: P.project_payload("PQ2_0_G128", rows, k6, pay6,
+                                                    gdn.forward_grouped(x6, d6)))
+        res["gdn_out_proj_grouped_step"] = {"gbs": round(pay6.size * reps / el / 1e9, 5),
+                                            "sample": "%d rows x %d" % (rows, k6)}
+        # prefill GEMM (config 5 recipe): 16 token rows x 256 weight rows
+        c = synth.make_config(5, n=rows, rows=16)
+        pay = codec.pack_rowsplit(c["fmt"], c["trits"], c["scale_bits"])
+        xr = T.forward(T.bf16_bits_to_f64(c["x"]), T.bf16_bits_to_f64(c["sign_bits"]))
+        reps, el = _timed(lambda: P.project_payload(c["fmt"], rows, c["k"], pay, xr))
+        res["cfg5_prefill_gemm"] = {"tflops": round(2.0 * 16 * rows * c["k"] * reps / el / 1e12, 6),
+                                    "sample": "16 x %d x %d" % (rows, c["k"])}
+    return res
 
 
 if __name__ == "__main__":
