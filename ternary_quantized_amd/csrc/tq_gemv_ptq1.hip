@@ -1,4 +1,4 @@
-// PTQ1_0_G128 decode GEMV on the matrix cores, batch 1..4 per launch pass:
+// PTQ1_0_G128 decode GEMV on the matrix cores, batch 1..8 per launch pass:
 //   y[b][n] = sum_g s[n][g] * sum_{j in g} t[n][j] * x'[b][j]
 // [ninfer-skill] §2-§3 (PTQ1_0: 24 base bytes + 2 high bytes + one fp16
 // scale per 128 weights, row-split planes); the trit packing inside the
@@ -14,9 +14,9 @@
 // lane l of wave w is lane j = l%4 of 4x4x4 MFMA block b = l/4 and owns
 // chunks (w*S + s)*16 + b, s < S, for the whole kernel; chunk counts that
 // do not fill W*S*16 slots leave "phantom" chunks with zero activations.
-// The lane keeps the binary16 activations of its chunks for batch row j in
-// registers and streams, for each row-quad, the chunk bytes of weight row
-// 4*rq + j.
+// The lane keeps the binary16 activations of its chunks for batch row j (and
+// 4 + j when eight rows are in flight) in registers and streams, for each
+// row-quad, the chunk bytes of weight row 4*rq + j.
 //
 // Decode: a 256-entry LDS table turns a byte into its five radix-3 digits
 // as 2-bit codes at bits 2i; two bytes side by side give, per digit i, a
@@ -25,7 +25,9 @@
 // exactly.  v_mfma_f32_4x4x4_16b_f16 then multiplies block b's four batch
 // rows (A, activations) by its four weight rows (B, trits) over 4 weights;
 // eight MFMAs cover a chunk, after which the chunk's group scale is
-// applied in fp32.  Partial sums are reduced over blocks with lane swaps
+// applied in fp32.  With eight batch rows a second set of eight MFMAs
+// reuses the same decoded trits for rows 4..7: the decode (vector ALU) is
+// what bounds the loop, so the second set costs little.  Partial sums are reduced over blocks with lane swaps
 // and DPP, over waves through LDS in a fixed order (no atomics: bitwise
 // reproducible).
 
@@ -105,12 +107,14 @@ __global__ __launch_bounds__(64 * W) void gemv_ptq1_kernel(Planes p, const void 
                                                            float *__restrict__ y, int64_t ldy,
                                                            Ptq1Shape sh) {
   constexpr int U = S * RR;  // steps per round (one ring of loads)
+  constexpr int NG = BT == 8 ? 2 : 1;     // groups of four batch rows in flight
+  constexpr int SB = BT == 1 ? 1 : 4;     // batch rows staged at a time
   __shared__ uint32_t lut[256];
   // per-wave activation staging (prologue), then the per-wave partial sums
-  // [row-quad][wave][j*4 + e] (epilogue)
-  constexpr int XST = W * BT * 512 * 2, RED = RQMAX * W * 16 * 4;
+  // [row-quad][wave][g*16 + j*4 + e] (epilogue)
+  constexpr int XST = W * SB * 512 * 2, RED = RQMAX * W * 16 * NG * 4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[XST > RED ? XST : RED];
-  uint16_t(*xst)[BT][512] = reinterpret_cast<uint16_t(*)[BT][512]>(lds);
+  uint16_t(*xst)[SB][512] = reinterpret_cast<uint16_t(*)[SB][512]>(lds);
   float *red = reinterpret_cast<float *>(lds);
 
   const int lane = threadIdx.x & 63;
@@ -168,10 +172,10 @@ __global__ __launch_bounds__(64 * W) void gemv_ptq1_kernel(Planes p, const void 
   // batch row through its own LDS with coalesced loads; lanes then pick
   // their chunk out of it.  Activations past k and batch rows past `batch`
   // are zero.
-  u32x2 xp[S][8];
+  u32x2 xp[NG][S][8];
   // activation loads first: a wave's loads complete in order, so loads
   // issued after the weight rows would wait for them
-  // (BT batch rows are loaded: 1 for a single row, else 4)
+  // (BT batch rows are loaded: 1 for a single row, else 4 or 8)
   u32x4 xraw[S][BT][XD == DT_F32 ? 2 : 1];
 #pragma unroll
   for (int s = 0; s < S; ++s) {
@@ -201,10 +205,15 @@ __global__ __launch_bounds__(64 * W) void gemv_ptq1_kernel(Planes p, const void 
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
   for (int s = 0; s < S; ++s) {
     const int e0 = (wave * S + s) * 512 + 8 * lane;
+    // a wave's LDS operations complete in order: the reads of the previous
+    // group are done before this group's writes reuse the staging rows
 #pragma unroll
-    for (int b = 0; b < BT; ++b) {
+    for (int bb = 0; bb < SB; ++bb) {
+      const int b = g * 4 + bb;
       const bool ok = b < batch && e0 < k32;
       uint32_t h[4];
       if constexpr (XD == DT_F16) {
@@ -227,10 +236,10 @@ __global__ __launch_bounds__(64 * W) void gemv_ptq1_kernel(Planes p, const void 
           h[t] = ok ? (uint32_t)f32_to_f16(v[2 * t]) | ((uint32_t)f32_to_f16(v[2 * t + 1]) << 16)
                     : 0u;
       }
-      *reinterpret_cast<u32x4 *>(&xst[wave][b][8 * lane]) = (u32x4){h[0], h[1], h[2], h[3]};
+      *reinterpret_cast<u32x4 *>(&xst[wave][bb][8 * lane]) = (u32x4){h[0], h[1], h[2], h[3]};
     }
-    // this lane's chunk blk of batch row j: 30 base trits at 128*(blk/4) +
-    // 30*(blk%4), 2 high trits at 128*(blk/4) + 120 + 2*(blk%4)
+    // this lane's chunk blk of batch row 4g + j: 30 base trits at
+    // 128*(blk/4) + 30*(blk%4), 2 high trits at 128*(blk/4) + 120 + 2*(blk%4)
     const uint32_t *src = reinterpret_cast<const uint32_t *>(&xst[wave][BT == 1 ? 0 : j][128 * (blk >> 2)]);
     uint32_t w[16];
 #pragma unroll
@@ -249,7 +258,8 @@ __global__ __launch_bounds__(64 * W) void gemv_ptq1_kernel(Planes p, const void 
     // (one staged row: lanes of batch rows 1..3 multiply by zero)
     const bool use = BT > 1 || j == 0;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) xp[s][m] = use ? (u32x2){pr[2 * m], pr[2 * m + 1]} : (u32x2){0u, 0u};
+    for (int m = 0; m < 8; ++m)
+      xp[g][s][m] = use ? (u32x2){pr[2 * m], pr[2 * m + 1]} : (u32x2){0u, 0u};
   }
 
 #pragma unroll
@@ -273,11 +283,13 @@ __global__ __launch_bounds__(64 * W) void gemv_ptq1_kernel(Planes p, const void 
   const half2_t neg2 = {(_Float16)-1025.0f, (_Float16)-1025.0f};
 
   auto do_round = [&](int rq0, auto refill, int valid) {
-    float yacc[RR][4];
+    float yacc[NG][RR][4];
 #pragma unroll
-    for (int r = 0; r < RR; ++r)
+    for (int g = 0; g < NG; ++g)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) yacc[r][e] = 0.0f;
+      for (int r = 0; r < RR; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yacc[g][r][e] = 0.0f;
     Rsrc next;
     if constexpr (decltype(refill)::value) next = rsrc_at(rq0 + RR);
 #pragma unroll
@@ -308,32 +320,55 @@ __global__ __launch_bounds__(64 * W) void gemv_ptq1_kernel(Planes p, const void 
       T[6] = (u32x2){trit_pair<2>(P2, magic_v), trit_pair<3>(P2, magic_v)};
       T[7] = (u32x2){trit_pair<4>(P2, magic_v),
                      u32(__builtin_elementwise_fma(h2(PH | magic_v), one2, neg2))};
-      // two independent accumulation chains
-      floatx4 a0 = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, xp[s][0]),
-                                                      __builtin_bit_cast(half4_t, T[0]),
-                                                      (floatx4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-      floatx4 a1 = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, xp[s][1]),
-                                                      __builtin_bit_cast(half4_t, T[1]),
-                                                      (floatx4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+      if constexpr (NG == 1) {
+        // two independent accumulation chains
+        floatx4 a0 = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, xp[0][s][0]),
+                                                        __builtin_bit_cast(half4_t, T[0]),
+                                                        (floatx4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        floatx4 a1 = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, xp[0][s][1]),
+                                                        __builtin_bit_cast(half4_t, T[1]),
+                                                        (floatx4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
-      for (int m = 2; m < 8; m += 2) {
-        a0 = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, xp[s][m]),
-                                                __builtin_bit_cast(half4_t, T[m]), a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, xp[s][m + 1]),
-                                                __builtin_bit_cast(half4_t, T[m + 1]), a1, 0, 0, 0);
+        for (int m = 2; m < 8; m += 2) {
+          a0 = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, xp[0][s][m]),
+                                                  __builtin_bit_cast(half4_t, T[m]), a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, xp[0][s][m + 1]),
+                                                  __builtin_bit_cast(half4_t, T[m + 1]), a1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yacc[0][r][e] += sc * (a0[e] + a1[e]);
+      } else {
+        // one chain per group of four batch rows (registers are short)
+        floatx4 a[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+          a[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, xp[g][s][0]),
+                                                    __builtin_bit_cast(half4_t, T[0]),
+                                                    (floatx4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+        for (int m = 1; m < 8; ++m)
+#pragma unroll
+          for (int g = 0; g < NG; ++g)
+            a[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, xp[g][s][m]),
+                                                      __builtin_bit_cast(half4_t, T[m]), a[g], 0, 0, 0);
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) yacc[g][r][e] += sc * a[g][e];
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) yacc[r][e] += sc * (a0[e] + a1[e]);
       __builtin_amdgcn_sched_barrier(0);
     }
     // per row-quad: sum over the wave's blocks, stash per wave
 #pragma unroll
     for (int r = 0; r < RR; ++r) {
       if (r >= valid) break;
-      const float tot = blocks_sum4(yacc[r]);
-      if ((lane & 12) == 0) {
-        const int e = (0x3120 >> (4 * (lane >> 4))) & 3;  // [0, 2, 1, 3][lane >> 4]
-        red[((rq0 + r) * W + wave) * 16 + j * 4 + e] = tot;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float tot = blocks_sum4(yacc[g][r]);
+        if ((lane & 12) == 0) {
+          const int e = (0x3120 >> (4 * (lane >> 4))) & 3;  // [0, 2, 1, 3][lane >> 4]
+          red[((rq0 + r) * W + wave) * (16 * NG) + g * 16 + j * 4 + e] = tot;
+        }
       }
     }
   };
@@ -345,14 +380,15 @@ __global__ __launch_bounds__(64 * W) void gemv_ptq1_kernel(Planes p, const void 
   __syncthreads();
 
   // ---- totals over waves, in wave order
-  for (int o = threadIdx.x; o < sh.rq * 16; o += blockDim.x) {
-    const int rq = o >> 4, jj = (o >> 2) & 3, e = o & 3;
+  for (int o = threadIdx.x; o < sh.rq * 16 * NG; o += blockDim.x) {
+    const int rq = o / (16 * NG), g = (o >> 4) % NG, jj = (o >> 2) & 3, e = o & 3;
     const int row = (rowq0 + rq) * 4 + jj;
-    if (row >= n32 || e >= batch) continue;
+    const int b = 4 * g + e;  // batch row
+    if (row >= n32 || b >= batch) continue;
     float sum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < W; ++w) sum += red[(rq * W + w) * 16 + jj * 4 + e];
-    y[(int64_t)e * ldy + row] = sum;
+    for (int w = 0; w < W; ++w) sum += red[(rq * W + w) * (16 * NG) + g * 16 + jj * 4 + e];
+    y[(int64_t)b * ldy + row] = sum;
   }
 }
 
@@ -365,9 +401,15 @@ hipError_t ptq1_go(const Planes &p, const void *x, int64_t batch, int64_t ldx, f
   if (batch <= 1)
     hipLaunchKernelGGL((gemv_ptq1_kernel<S, RR, W, XD, 1>), dim3((unsigned)grid), dim3(64 * W), 0,
                        st, p, x, batch, ldx, y, ldy, sh);
-  else
+  else if (batch <= 4)
     hipLaunchKernelGGL((gemv_ptq1_kernel<S, RR, W, XD, 4>), dim3((unsigned)grid), dim3(64 * W), 0,
                        st, p, x, batch, ldx, y, ldy, sh);
+  else if constexpr (S <= 3 && XD != DT_F32)
+    // eight rows: their activations take the registers of a deeper ring
+    hipLaunchKernelGGL((gemv_ptq1_kernel<S, 1, W, XD, 8>), dim3((unsigned)grid), dim3(64 * W), 0,
+                       st, p, x, batch, ldx, y, ldy, sh);
+  else
+    return hipErrorInvalidValue;  // not reached: such passes hold at most four rows
   return hipGetLastError();
 }
 
@@ -379,14 +421,28 @@ hipError_t ptq1_dt(const Planes &p, const void *x, int xd, int64_t batch, int64_
   return ptq1_go<S, RR, W, DT_F16>(p, x, batch, ldx, y, ldy, rq, grid, st);
 }
 
-// One pass of up to four batch rows.
+// Waves per workgroup (up to twelve, fewer for short rows: a wave covers 16
+// chunks a slot) and slots per lane for k/32 chunks.
+void ptq1_split(int chunks, int &W, int &S) {
+  const int cw = (chunks + 15) / 16;
+  W = cw <= 4 ? 4 : cw <= 8 ? 8 : 12;
+  S = (chunks + 16 * W - 1) / (16 * W);
+}
+
+// Batch rows one pass can hold: eight where the activations of eight rows
+// fit the registers (up to three slots, 16-bit activations), else four.
+int ptq1_pass_rows(const Planes &p, int xd) {
+  int W, S;
+  ptq1_split((int)(p.k / 32), W, S);
+  return S <= 3 && xd != DT_F32 ? 8 : 4;
+}
+
+// One pass of up to ptq1_pass_rows batch rows.
 hipError_t ptq1_pass(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx, float *y,
                      int64_t ldy, hipStream_t st) {
   const int chunks = (int)(p.k / 32);
-  // waves: up to twelve, fewer for short rows (a wave covers 16 chunks a slot)
-  const int cw = (chunks + 15) / 16;
-  const int W = cw <= 4 ? 4 : cw <= 8 ? 8 : 12;
-  const int S = (chunks + 16 * W - 1) / (16 * W);
+  int W, S;
+  ptq1_split(chunks, W, S);
   // row-quads per workgroup: an equal share per compute unit, at most RQMAX
   const int cus = device_cus();
   const int64_t nq = (p.n + 3) / 4;
@@ -421,8 +477,9 @@ bool gemv_ptq1_fits(const Planes &p) {
 hipError_t launch_gemv_ptq1(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx,
                             float *y, int64_t ldy, hipStream_t st) {
   const int64_t esz = xd == DT_F32 ? 4 : 2;
-  for (int64_t b0 = 0; b0 < batch; b0 += 4) {
-    const int64_t nb = batch - b0 < 4 ? batch - b0 : 4;
+  const int64_t step = ptq1_pass_rows(p, xd);
+  for (int64_t b0 = 0; b0 < batch; b0 += step) {
+    const int64_t nb = batch - b0 < step ? batch - b0 : step;
     hipError_t e = ptq1_pass(p, static_cast<const char *>(x) + b0 * ldx * esz, xd, nb, ldx,
                              y + b0 * ldy, ldy, st);
     if (e != hipSuccess) return e;
