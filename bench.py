@@ -298,10 +298,27 @@ def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream):
         del gcps
         torch.cuda.empty_cache()
 
-        # config 2 shape expanded to G64 (+6% bytes over PQ2_0), batch 1
+        # config 2 shape at batch 4 and 8 (row-quad MFMA GEMV), then expanded
+        # to G64 (+6% bytes over PQ2_0) at batch 1
         c2 = synth.make_config(2)
-        p2 = to_dev(tq.pack_rowsplit(c2["fmt"], c2["trits"], c2["scale_bits"]))
+        p2h = tq.pack_rowsplit(c2["fmt"], c2["trits"], c2["scale_bits"])
         n2, k2 = c2["n"], c2["k"]
+        nc2 = copies_for(p2h.size)
+        cps2 = [to_dev(p2h)]
+        cps2 += [cps2[0].clone() for _ in range(nc2 - 1)]
+        x2b = bits_dev(synth.activations_bf16_bits(np.random.default_rng(22), 8, k2), torch.bfloat16)
+        s2b = bits_dev(c2["sign_bits"], torch.bfloat16)
+        for b in (4, 8):
+            xr = tq.hadamard_signed(x2b[:b], s2b, out_dtype=torch.float16)
+            yb = torch.empty((b, n2), dtype=torch.float32, device=xr.device)
+            mean = event_timed(torch, lambda i: tq.gemv_rowsplit(cps2[i % nc2], c2["fmt"], n2, k2, xr,
+                                                                  out=yb), 4 * nc2)
+            byts = p2h.size + 2 * b * k2 + 4 * b * n2
+            res["cfg2_shape_pq2_b%d" % b] = {"mean_launch_us": round(mean * 1e6, 3),
+                                             "gbs": round(byts / mean / 1e9, 1),
+                                             "frac_hbm": round(byts / mean / 1e9 / HBM_PEAK_GBS, 4)}
+        p2 = cps2[0]
+        del cps2
         gbytes = tq.g64_bytes(n2, k2)
         gcps = [tq.expand_g64(p2, c2["fmt"], n2, k2) for _ in range(copies_for(gbytes))]
         x2 = bits_dev(c2["x"], torch.bfloat16)

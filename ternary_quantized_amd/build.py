@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
 BUILD = os.path.join(HERE, "_build")
 
-HIP_SOURCES = ["tq_hadamard.hip", "tq_gemv.hip", "tq_gemv_ptq1.hip", "tq_gemm.hip",
+HIP_SOURCES = ["tq_hadamard.hip", "tq_gemv.hip", "tq_gemv_quads.hip", "tq_gemm.hip",
                "tq_transcode.hip", "tq_q2g64.hip", "tq_head.hip"]
 HOST_SOURCES = ["tq_host.cpp", "tq_container.cpp"]
 

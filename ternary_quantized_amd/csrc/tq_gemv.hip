@@ -543,185 +543,6 @@ static hipError_t gemv_wave(const Planes &p, const void *x, int xd, const uint16
   }
 }
 
-// ---------------------------------------------------------------------------
-// PQ2_0 GEMV on the matrix cores (batch 1..4).
-//
-// v_mfma_f32_4x4x4_16b_f16 multiplies 16 independent 4x4x4 blocks; block q of
-// a wave is lanes 4q..4q+3.  Here a block is one activation chunk of 64
-// weights shared by 4 weight rows: lane 4q+j supplies 4 consecutive (in
-// decode order) weights of row j as the B operand and the matching 4
-// activations of batch row j (batch 1: the same row in all four lanes) as
-// the A operand.  Output element [i][j] of a block is then
-// sum_k x_i[k] * w_j[k] over the chunk; with batch 1 every i is the same
-// activation row, so the element at index lane%4 is row (lane%4)'s partial
-// sum whichever way the block's output is laid out over its lanes.
-//
-// Codes are decoded exactly to binary16 trits with full-rate integer ops:
-// OR-ing a code at mantissa bits 2e (e <= 4) into the exponent of 1024
-// gives 1024 + 4^e * code, and one packed fma with (1/4^e, -(1024/4^e + 1))
-// turns that into code - 1 exactly; codes in bits 10..15 are shifted down
-// first.  A dword of 16 codes takes 9 bit operations and 8 packed fmas.
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-// (d & mask) | magic in one v_and_or_b32 (magic held in a VGPR: a VOP3
-// instruction takes at most one literal/SGPR operand here).
-__device__ __forceinline__ uint32_t and_or(uint32_t d, uint32_t mask, uint32_t magic_v) {
-  return (d & mask) | magic_v;
-}
-
-// Two masked code pairs -> 4 trits (binary16) for one MFMA B operand.
-// t = 1024 + m*code (exact); fma(t, 1/m, -(1024/m + 1)) = code - 1 (exact).
-__device__ __forceinline__ half4_t trit4(uint32_t ta, uint32_t tb, float inv_ma, float neg_ca,
-                                         float inv_mb, float neg_cb) {
-  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-  const u32x2_t tt = {ta, tb};
-  const half4_t t4 = __builtin_bit_cast(half4_t, tt);
-  const half4_t m4 = {(_Float16)inv_ma, (_Float16)inv_ma, (_Float16)inv_mb, (_Float16)inv_mb};
-  const half4_t c4 = {(_Float16)neg_ca, (_Float16)neg_ca, (_Float16)neg_cb, (_Float16)neg_cb};
-  return __builtin_elementwise_fma(t4, m4, c4);
-}
-
-// 16 codes of dword d -> 4 MFMA B operands; operand h holds the trits of
-// codes (2h, 2h+8, 2h+1, 2h+9).
-__device__ __forceinline__ void decode_pq2_trit4(uint32_t d, uint32_t magic_v, half4_t w[4]) {
-  const uint32_t d10 = d >> 10;
-  w[0] = trit4(and_or(d, 0x00030003u, magic_v), and_or(d, 0x000C000Cu, magic_v),
-               1.0f, -1025.0f, 0.25f, -257.0f);
-  w[1] = trit4(and_or(d, 0x00300030u, magic_v), and_or(d, 0x00C000C0u, magic_v),
-               0.0625f, -65.0f, 0.015625f, -17.0f);
-  w[2] = trit4(and_or(d, 0x03000300u, magic_v), and_or(d10, 0x00030003u, magic_v),
-               0.00390625f, -5.0f, 1.0f, -1025.0f);
-  w[3] = trit4(and_or(d10, 0x000C000Cu, magic_v), and_or(d10, 0x00300030u, magic_v),
-               0.25f, -257.0f, 0.0625f, -65.0f);
-}
-
-// Lane layout: thread t of the workgroup is lane j = t % 4 of block
-// q = t / 4; blocks [team*cpad, team*cpad + chunks) hold the chunks of team
-// `team`, each team covering 4 rows per pass.  cpad = chunks rounded up to a
-// multiple of 4 (whole 16-lane segments).
-template <int P, int XD, bool BATCHED>
-__global__ __launch_bounds__(1024) void gemv_mfma_kernel(Planes p, const void *__restrict__ x,
-                                                         int64_t batch, int64_t ldx,
-                                                         float *__restrict__ y, int64_t ldy,
-                                                         int chunks, int cpad, int teams) {
-  __shared__ float red[P * (BATCHED ? 4 : 1) * 64 * 4];  // [pass][batch][segment][row j]
-  const int t = threadIdx.x;
-  const int j = t & 3;
-  const int q = t >> 2;
-  const int team = q / cpad;
-  const int c = q % cpad;
-  const bool active = team < teams && c < chunks;
-  const int64_t rows_per_pass = 4 * (int64_t)teams;
-  const int64_t row_base = (int64_t)blockIdx.x * rows_per_pass * P + 4 * team + j;
-
-  // ---- weight loads for all P passes (16 bytes = 64 codes per lane)
-  u32x4 raw[P];
-  uint32_t sraw[P];
-  const uint8_t *wp = p.base + row_base * p.base_row + c * 16;
-  const uint16_t *sp = p.scale + row_base * p.groups + (c >> 1);
-  const int64_t wstep = rows_per_pass * p.base_row, sstep = rows_per_pass * p.groups;
-#pragma unroll
-  for (int it = 0; it < P; ++it) {
-    if (active && row_base + it * rows_per_pass < p.n) {
-      raw[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wp + it * wstep));
-      sraw[it] = sp[it * sstep];
-    }
-  }
-
-  // ---- activations of the chunk as the A operand, in decode order:
-  // dword d, pair e = (16d + e, 16d + e + 8); MFMA step (d, h) uses pairs
-  // 2h, 2h+1.  Batched: lane j carries batch row j (zero beyond batch).
-  half4_t xa[16];  // A operand of MFMA step (dword d, h): xa[4d + h]
-  {
-    const int b = BATCHED ? j : 0;
-    const bool xok = active && b < batch;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      float v[16];
-      if (xok) {
-        load16<XD>(x, b * ldx + (int64_t)c * 64 + 16 * d, v);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = 0.0f;
-      }
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int e = 2 * h;
-        xa[4 * d + h] = (half4_t){(_Float16)v[e], (_Float16)v[e + 8], (_Float16)v[e + 1],
-                                  (_Float16)v[e + 9]};
-      }
-    }
-  }
-  uint32_t magic_v = 0x64006400u;
-  asm volatile("" : "+v"(magic_v));
-
-  const int seg = t >> 4;
-#pragma unroll
-  for (int it = 0; it < P; ++it) {
-    const bool ok = active && row_base + it * rows_per_pass < p.n;
-    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    float s = 0.0f;
-    if (ok) {
-      const uint32_t dw[4] = {raw[it][0], raw[it][1], raw[it][2], raw[it][3]};
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        half4_t w[4];
-        decode_pq2_trit4(dw[d], magic_v, w);
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-          acc = __builtin_amdgcn_mfma_f32_4x4x4f16(xa[4 * d + h], w[h], acc, 0, 0, 0);
-      }
-      s = f16_to_f32(sraw[it]);
-    }
-    // batch 1: element j is row j's partial; batched: lane j of the block
-    // holds its column's four batch rows (elements) -- reduced below per
-    // element.
-    if constexpr (!BATCHED) {
-      float v = j == 0 ? acc[0] : j == 1 ? acc[1] : j == 2 ? acc[2] : acc[3];
-      v *= s;
-      // sum the 4 blocks of this 16-lane segment (lanes with equal j)
-      v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                         0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF, true));
-      v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                         0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF, true));
-      if ((t & 15) >= 12) red[(it * 64 + seg) * 4 + j] = v;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float v = acc[e] * s;
-        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                           0, __builtin_bit_cast(int, v), 0x114, 0xF, 0xF, true));
-        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
-                                           0, __builtin_bit_cast(int, v), 0x118, 0xF, 0xF, true));
-        acc[e] = v;
-      }
-      // lane 12+j holds (batch e, row j) sums of its segment; stash them
-      if ((t & 15) >= 12) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) red[((it * 4 + e) * 64 + seg) * 4 + j] = acc[e];
-      }
-    }
-  }
-  __syncthreads();
-  const int segs = cpad >> 2;
-  const int nb = BATCHED ? 4 : 1;
-  for (int o = t; o < P * teams * 4 * nb; o += blockDim.x) {
-    const int jj = o & 3;
-    const int rest = o >> 2;
-    const int b = rest % nb;
-    const int tm = (rest / nb) % teams;
-    const int it = rest / (nb * teams);
-    const int64_t row = (int64_t)blockIdx.x * rows_per_pass * P + it * rows_per_pass + 4 * tm + jj;
-    if (row >= p.n || b >= batch) continue;
-    const float *rp = BATCHED ? red + ((it * 4 + b) * 64 + tm * segs) * 4 + jj
-                              : red + (it * 64 + tm * segs) * 4 + jj;
-    float sum = 0.0f;
-    for (int sgi = 0; sgi < segs; ++sgi) sum += rp[4 * sgi];
-    y[b * ldy + row] = sum;
-  }
-}
-
 // Teams per workgroup: fewest idle lanes, then the smallest workgroup.
 // Workgroups stay within 512 lanes whenever one team fits, so the kernel
 // can be compiled for a 512-lane bound (more registers per lane).
@@ -806,41 +627,6 @@ static hipError_t gemv_b1(const Planes &p, const void *x, int xd, int64_t ldx, f
   return gemv_go<FMT, CW, 1, 4>(p, x, xd, 1, ldx, y, ldy, st);
 }
 
-template <int P, bool BATCHED>
-static hipError_t gemv_mfma_go(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx,
-                               float *y, int64_t ldy, hipStream_t st) {
-  const int chunks = (int)(p.k / 64);
-  const int cpad = (chunks + 3) / 4 * 4;
-  const int teams = pick_teams(4 * cpad);
-  const int threads = (teams * 4 * cpad + 63) / 64 * 64;
-  const int64_t rows_per_wg = 4LL * teams * P;
-  dim3 grid((unsigned)((p.n + rows_per_wg - 1) / rows_per_wg)), block(threads);
-  if (xd == DT_F32)
-    hipLaunchKernelGGL((gemv_mfma_kernel<P, DT_F32, BATCHED>), grid, block, 0, st, p, x, batch, ldx,
-                       y, ldy, chunks, cpad, teams);
-  else if (xd == DT_BF16)
-    hipLaunchKernelGGL((gemv_mfma_kernel<P, DT_BF16, BATCHED>), grid, block, 0, st, p, x, batch, ldx,
-                       y, ldy, chunks, cpad, teams);
-  else
-    hipLaunchKernelGGL((gemv_mfma_kernel<P, DT_F16, BATCHED>), grid, block, 0, st, p, x, batch, ldx,
-                       y, ldy, chunks, cpad, teams);
-  return hipGetLastError();
-}
-
-// PQ2_0 rows of up to 16384 weights run on the matrix cores (a team of
-// 4 * ceil(k/256) * 4 lanes must fit a 1024-lane workgroup).
-static bool gemv_mfma_fits(const Planes &p) { return p.k <= 16384; }
-
-template <bool BATCHED>
-static hipError_t gemv_mfma(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx,
-                            float *y, int64_t ldy, hipStream_t st) {
-  const int cpad = ((int)(p.k / 64) + 3) / 4 * 4;
-  const int64_t passes = (p.n + 4LL * pick_teams(4 * cpad) - 1) / (4LL * pick_teams(4 * cpad));
-  if (passes >= 512 * 8) return gemv_mfma_go<8, BATCHED>(p, x, xd, batch, ldx, y, ldy, st);
-  return gemv_mfma_go<4, BATCHED>(p, x, xd, batch, ldx, y, ldy, st);
-}
-
-// Largest supported k: a team of at most 1024 lanes must cover a row.
 int64_t gemv_max_k(int fmt) { return fmt == FMT_PQ2 ? 64 * 1024 : 32 * 1024; }
 
 // Lane chunk (CW weights), batch tile (B) and rows per thread (P) by batch:
@@ -849,7 +635,7 @@ int64_t gemv_max_k(int fmt) { return fmt == FMT_PQ2 ? 64 * 1024 : 32 * 1024; }
 hipError_t launch_gemv(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx,
                        float *y, int64_t ldy, hipStream_t st) {
   if (p.fmt == FMT_PTQ1) {
-    if (gemv_ptq1_fits(p)) return launch_gemv_ptq1(p, x, xd, batch, ldx, y, ldy, st);
+    if (gemv_quads_fits(p)) return launch_gemv_quads(p, x, xd, batch, ldx, y, ldy, st);
     if (batch <= 1) return gemv_b1<FMT_PTQ1, 32>(p, x, xd, ldx, y, ldy, st);
     if (batch <= 2) return gemv_go<FMT_PTQ1, 32, 2, 4>(p, x, xd, batch, ldx, y, ldy, st);
     if (batch <= 4) return gemv_go<FMT_PTQ1, 32, 4, 2>(p, x, xd, batch, ldx, y, ldy, st);
@@ -866,8 +652,7 @@ hipError_t launch_gemv(const Planes &p, const void *x, int xd, int64_t batch, in
   }
   // a chunk never spans two groups (64 | 128); wide rows need wider chunks
   const bool wide32 = p.k / 32 > 1024, wide16 = p.k / 16 > 1024;
-  if (gemv_mfma_fits(p) && batch >= 2 && batch <= 4)
-    return gemv_mfma<true>(p, x, xd, batch, ldx, y, ldy, st);
+  if (batch >= 2 && gemv_quads_fits(p)) return launch_gemv_quads(p, x, xd, batch, ldx, y, ldy, st);
   if (batch <= 1 && gemv_wave_fits(p)) return gemv_wave<false>(p, x, xd, nullptr, y, st);
   if (batch <= 1 || (wide32 && batch <= 2)) {
     if (batch <= 1) return gemv_b1<FMT_PQ2, 64>(p, x, xd, ldx, y, ldy, st);

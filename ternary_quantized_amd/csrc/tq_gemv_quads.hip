@@ -1,14 +1,18 @@
-// PTQ1_0_G128 decode GEMV on the matrix cores, batch 1..8 per launch pass:
+// Decode GEMV on the matrix cores over row-quads, batch 1..8 per launch
+// pass (PTQ1_0_G128 at every batch, PQ2_0_G128 at batch 2..8):
 //   y[b][n] = sum_g s[n][g] * sum_{j in g} t[n][j] * x'[b][j]
-// [ninfer-skill] §2-§3 (PTQ1_0: 24 base bytes + 2 high bytes + one fp16
-// scale per 128 weights, row-split planes); the trit packing inside the
-// bytes is this library's convention (five radix-3 digits per base byte,
-// four per high byte, least significant digit first), stated in tq.h.
+// [ninfer-skill] §2-§3 (row-split planes; PTQ1_0: 24 base bytes + 2 high
+// bytes + one fp16 scale per 128 weights, PQ2_0: 32 base bytes + the
+// scale); [gguf-explainer] §4.3 (PQ2_0 codes: weight j at byte j/4, bits
+// 2*(j%4), value code-1).  The PTQ1_0 trit packing inside the bytes is this
+// library's convention (five radix-3 digits per base byte, four per high
+// byte, least significant digit first), stated in tq.h.
 //
 // Work split (gfx950, wave64).  A row of k weights is cut into 32-weight
-// chunks: quarter q of group g holds base bytes 6q..6q+5 (trits 30q..30q+29
-// of the group) and digits 2(q&1), 2(q&1)+1 of high byte q>>1 (trits
-// 120+2q, 121+2q).  A workgroup owns RQ consecutive row-quads (4 rows each)
+// chunks: quarter q of group g holds, for PTQ1_0, base bytes 6q..6q+5
+// (trits 30q..30q+29 of the group) and digits 2(q&1), 2(q&1)+1 of high byte
+// q>>1 (trits 120+2q, 121+2q); for PQ2_0, base bytes 8q..8q+7 (weights
+// 32q..32q+31).  A workgroup owns RQ consecutive row-quads (4 rows each)
 // over the whole of k, so every CU gets the same number of rows and no
 // result leaves the workgroup unfinished.  Its W waves split the chunks:
 // lane l of wave w is lane j = l%4 of 4x4x4 MFMA block b = l/4 and owns
@@ -18,11 +22,13 @@
 // 4 + j when eight rows are in flight) in registers and streams, for each
 // row-quad, the chunk bytes of weight row 4*rq + j.
 //
-// Decode: a 256-entry LDS table turns a byte into its five radix-3 digits
-// as 2-bit codes at bits 2i; two bytes side by side give, per digit i, a
-// pair of codes that one and-or places into the mantissa of binary16 1024
-// (1024 + 4^i * code) and one packed fma turns into the trit code - 1
-// exactly.  v_mfma_f32_4x4x4_16b_f16 then multiplies block b's four batch
+// Decode: PTQ1_0 -- a 256-entry LDS table turns a byte into its five
+// radix-3 digits as 2-bit codes at bits 2i; two bytes side by side give,
+// per digit i, a pair of codes.  PQ2_0 -- a dword of 16 codes holds codes e
+// and e+8 at bits 2e of its two halves (e <= 4; codes 5..7 and 13..15 after
+// a shift by 10).  Either way one and-or places a code pair into the
+// mantissa of binary16 1024 (1024 + 4^i * code) and one packed fma turns it
+// into the trit pair code - 1 exactly.  v_mfma_f32_4x4x4_16b_f16 then multiplies block b's four batch
 // rows (A, activations) by its four weight rows (B, trits) over 4 weights;
 // eight MFMAs cover a chunk, after which the chunk's group scale is
 // applied in fp32.  With eight batch rows a second set of eight MFMAs
@@ -101,8 +107,8 @@ struct Ptq1Shape {
   int rq;      // row-quads per workgroup (a multiple of RR)
 };
 
-template <int S, int RR, int W, int XD, int BT>
-__global__ __launch_bounds__(64 * W) void gemv_ptq1_kernel(Planes p, const void *__restrict__ x,
+template <int FMT, int S, int RR, int W, int XD, int BT>
+__global__ __launch_bounds__(64 * W) void gemv_quads_kernel(Planes p, const void *__restrict__ x,
                                                            int64_t batch, int64_t ldx,
                                                            float *__restrict__ y, int64_t ldy,
                                                            Ptq1Shape sh) {
@@ -134,8 +140,13 @@ __global__ __launch_bounds__(64 * W) void gemv_ptq1_kernel(Planes p, const void 
     real[s] = c0 < sh.chunks;
     const int c = real[s] ? c0 : 0;
     const int g = c >> 2, q = c & 3;
-    ob[s] = j * (int)p.base_row + g * 24 + ((6 * q) & ~3);
-    oh[s] = j * (int)p.high_row + g * 2 + (q >> 1);
+    if constexpr (FMT == FMT_PTQ1) {
+      ob[s] = j * (int)p.base_row + g * 24 + ((6 * q) & ~3);
+      oh[s] = j * (int)p.high_row + g * 2 + (q >> 1);
+    } else {
+      ob[s] = j * (int)p.base_row + g * 32 + 8 * q;
+      oh[s] = 0;
+    }
     os[s] = (j * (int)p.groups + g) * 2;
   }
   const int q = blk & 3;  // every chunk of this lane has the same quarter (16 | chunk stride)
@@ -161,7 +172,8 @@ __global__ __launch_bounds__(64 * W) void gemv_ptq1_kernel(Planes p, const void 
   auto load_step = [&](const Rsrc &r, int s, ChunkRaw &c) {
     c.w0 = __builtin_amdgcn_raw_buffer_load_b32(r.b, ob[s], 0, 2);
     c.w1 = __builtin_amdgcn_raw_buffer_load_b32(r.b, ob[s] + 4, 0, 2);
-    c.h = __builtin_amdgcn_raw_buffer_load_b8(r.h, oh[s], 0, 2);
+    if constexpr (FMT == FMT_PTQ1) c.h = __builtin_amdgcn_raw_buffer_load_b8(r.h, oh[s], 0, 2);
+    else c.h = 0;
     c.s = __builtin_amdgcn_raw_buffer_load_b16(r.s, os[s], 0, 0);
   };
 
@@ -238,23 +250,38 @@ __global__ __launch_bounds__(64 * W) void gemv_ptq1_kernel(Planes p, const void 
       }
       *reinterpret_cast<u32x4 *>(&xst[wave][bb][8 * lane]) = (u32x4){h[0], h[1], h[2], h[3]};
     }
-    // this lane's chunk blk of batch row 4g + j: 30 base trits at
-    // 128*(blk/4) + 30*(blk%4), 2 high trits at 128*(blk/4) + 120 + 2*(blk%4)
+    // this lane's chunk blk of batch row 4g + j.  PTQ1_0: 30 base trits at
+    // 128*(blk/4) + 30*(blk%4), 2 high trits at 128*(blk/4) + 120 + 2*(blk%4);
+    // PQ2_0: 32 consecutive weights at 32*blk
     const uint32_t *src = reinterpret_cast<const uint32_t *>(&xst[wave][BT == 1 ? 0 : j][128 * (blk >> 2)]);
     uint32_t w[16];
+    if constexpr (FMT == FMT_PTQ1) {
 #pragma unroll
-    for (int t = 0; t < 15; ++t) w[t] = src[15 * q + t];
-    w[15] = src[60 + q];
-    // w[t] holds trits 2t, 2t+1 of the chunk (t < 15) and the high pair
+      for (int t = 0; t < 15; ++t) w[t] = src[15 * q + t];
+      w[15] = src[60 + q];
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) w[t] = src[16 * q + t];
+    }
+    // w[t] holds weights 2t, 2t+1 of the chunk (PTQ1_0: t < 15, then the
+    // high pair)
     auto el = [&](int i) -> uint32_t {  // trit i (< 30) of the chunk, binary16 bits
       return (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
     };
     uint32_t pr[16];
+    if constexpr (FMT == FMT_PTQ1) {
 #pragma unroll
-    for (int pp = 0; pp < 3; ++pp)
+      for (int pp = 0; pp < 3; ++pp)
 #pragma unroll
-      for (int i = 0; i < 5; ++i) pr[5 * pp + i] = el(10 * pp + i) | (el(10 * pp + 5 + i) << 16);
-    pr[15] = w[15];
+        for (int i = 0; i < 5; ++i) pr[5 * pp + i] = el(10 * pp + i) | (el(10 * pp + 5 + i) << 16);
+      pr[15] = w[15];
+    } else {
+      // pair 8d + e = weights (16d + e, 16d + e + 8) of the chunk
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pr[8 * d + e] = el(16 * d + e) | (el(16 * d + e + 8) << 16);
+    }
     // (one staged row: lanes of batch rows 1..3 multiply by zero)
     const bool use = BT > 1 || j == 0;
 #pragma unroll
@@ -269,8 +296,8 @@ __global__ __launch_bounds__(64 * W) void gemv_ptq1_kernel(Planes p, const void 
     for (int s = 0; s < S; ++s) load_step(rr, s, ring[r * S + s]);
   }
 
-  // ---- the digit table
-  for (int v = threadIdx.x; v < 256; v += blockDim.x) {
+  // ---- the digit table (PTQ1_0)
+  for (int v = threadIdx.x; v < (FMT == FMT_PTQ1 ? 256 : 0); v += blockDim.x) {
     uint32_t a = (uint32_t)v, w = 0;
     for (int i = 0; i < 5; ++i) { w |= (a % 3u) << (2 * i); a /= 3u; }
     lut[v] = w;
@@ -301,25 +328,38 @@ __global__ __launch_bounds__(64 * W) void gemv_ptq1_kernel(Planes p, const void 
         if (u % S == 0 && u > 0) next = rsrc_at(rq0 + RR + r);
         load_step(next, s, ring[u]);
       }
-      // the six base bytes and the high byte through the digit table
-      const uint64_t win = (((uint64_t)c.w1 << 32) | c.w0) >> bshift;
-      const uint32_t lo = (uint32_t)win, hi = (uint32_t)(win >> 32);
-      const uint32_t P0 = lut[lo & 0xFF] | (lut[(lo >> 8) & 0xFF] << 16);
-      const uint32_t P1 = lut[(lo >> 16) & 0xFF] | (lut[lo >> 24] << 16);
-      const uint32_t P2 = lut[hi & 0xFF] | (lut[(hi >> 8) & 0xFF] << 16);
-      const uint32_t L = lut[c.h & 0xFF] >> hshift;
-      const uint32_t PH = (L & 3u) | ((L & 0xCu) << 14);
       const float sc = real[s] ? f16_to_f32((uint16_t)c.s) : 0.0f;
       u32x2 T[8];
-      T[0] = (u32x2){trit_pair<0>(P0, magic_v), trit_pair<1>(P0, magic_v)};
-      T[1] = (u32x2){trit_pair<2>(P0, magic_v), trit_pair<3>(P0, magic_v)};
-      T[2] = (u32x2){trit_pair<4>(P0, magic_v), trit_pair<0>(P1, magic_v)};
-      T[3] = (u32x2){trit_pair<1>(P1, magic_v), trit_pair<2>(P1, magic_v)};
-      T[4] = (u32x2){trit_pair<3>(P1, magic_v), trit_pair<4>(P1, magic_v)};
-      T[5] = (u32x2){trit_pair<0>(P2, magic_v), trit_pair<1>(P2, magic_v)};
-      T[6] = (u32x2){trit_pair<2>(P2, magic_v), trit_pair<3>(P2, magic_v)};
-      T[7] = (u32x2){trit_pair<4>(P2, magic_v),
-                     u32(__builtin_elementwise_fma(h2(PH | magic_v), one2, neg2))};
+      if constexpr (FMT == FMT_PTQ1) {
+        // the six base bytes and the high byte through the digit table
+        const uint64_t win = (((uint64_t)c.w1 << 32) | c.w0) >> bshift;
+        const uint32_t lo = (uint32_t)win, hi = (uint32_t)(win >> 32);
+        const uint32_t P0 = lut[lo & 0xFF] | (lut[(lo >> 8) & 0xFF] << 16);
+        const uint32_t P1 = lut[(lo >> 16) & 0xFF] | (lut[lo >> 24] << 16);
+        const uint32_t P2 = lut[hi & 0xFF] | (lut[(hi >> 8) & 0xFF] << 16);
+        const uint32_t L = lut[c.h & 0xFF] >> hshift;
+        const uint32_t PH = (L & 3u) | ((L & 0xCu) << 14);
+        T[0] = (u32x2){trit_pair<0>(P0, magic_v), trit_pair<1>(P0, magic_v)};
+        T[1] = (u32x2){trit_pair<2>(P0, magic_v), trit_pair<3>(P0, magic_v)};
+        T[2] = (u32x2){trit_pair<4>(P0, magic_v), trit_pair<0>(P1, magic_v)};
+        T[3] = (u32x2){trit_pair<1>(P1, magic_v), trit_pair<2>(P1, magic_v)};
+        T[4] = (u32x2){trit_pair<3>(P1, magic_v), trit_pair<4>(P1, magic_v)};
+        T[5] = (u32x2){trit_pair<0>(P2, magic_v), trit_pair<1>(P2, magic_v)};
+        T[6] = (u32x2){trit_pair<2>(P2, magic_v), trit_pair<3>(P2, magic_v)};
+        T[7] = (u32x2){trit_pair<4>(P2, magic_v),
+                       u32(__builtin_elementwise_fma(h2(PH | magic_v), one2, neg2))};
+      } else {
+        // codes e and e+8 of each dword: in place for e <= 4, after a shift
+        // by 10 for e = 5..7
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const uint32_t v = d ? c.w1 : c.w0, v10 = v >> 10;
+          T[4 * d + 0] = (u32x2){trit_pair<0>(v, magic_v), trit_pair<1>(v, magic_v)};
+          T[4 * d + 1] = (u32x2){trit_pair<2>(v, magic_v), trit_pair<3>(v, magic_v)};
+          T[4 * d + 2] = (u32x2){trit_pair<4>(v, magic_v), trit_pair<0>(v10, magic_v)};
+          T[4 * d + 3] = (u32x2){trit_pair<1>(v10, magic_v), trit_pair<2>(v10, magic_v)};
+        }
+      }
       if constexpr (NG == 1) {
         // two independent accumulation chains
         floatx4 a0 = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, xp[0][s][0]),
@@ -392,38 +432,45 @@ __global__ __launch_bounds__(64 * W) void gemv_ptq1_kernel(Planes p, const void 
   }
 }
 
-template <int S, int RR, int W, int XD>
-hipError_t ptq1_go(const Planes &p, const void *x, int64_t batch, int64_t ldx, float *y,
+template <int FMT, int S, int RR, int W, int XD>
+hipError_t quads_go(const Planes &p, const void *x, int64_t batch, int64_t ldx, float *y,
                    int64_t ldy, int rq, int grid, hipStream_t st) {
   Ptq1Shape sh;
   sh.chunks = (int)(p.k / 32);
   sh.rq = rq;
   if (batch <= 1)
-    hipLaunchKernelGGL((gemv_ptq1_kernel<S, RR, W, XD, 1>), dim3((unsigned)grid), dim3(64 * W), 0,
+    hipLaunchKernelGGL((gemv_quads_kernel<FMT, S, RR, W, XD, 1>), dim3((unsigned)grid), dim3(64 * W), 0,
                        st, p, x, batch, ldx, y, ldy, sh);
   else if (batch <= 4)
-    hipLaunchKernelGGL((gemv_ptq1_kernel<S, RR, W, XD, 4>), dim3((unsigned)grid), dim3(64 * W), 0,
+    hipLaunchKernelGGL((gemv_quads_kernel<FMT, S, RR, W, XD, 4>), dim3((unsigned)grid), dim3(64 * W), 0,
                        st, p, x, batch, ldx, y, ldy, sh);
   else if constexpr (S <= 3 && XD != DT_F32)
     // eight rows: their activations take the registers of a deeper ring
-    hipLaunchKernelGGL((gemv_ptq1_kernel<S, 1, W, XD, 8>), dim3((unsigned)grid), dim3(64 * W), 0,
+    hipLaunchKernelGGL((gemv_quads_kernel<FMT, S, 1, W, XD, 8>), dim3((unsigned)grid), dim3(64 * W), 0,
                        st, p, x, batch, ldx, y, ldy, sh);
   else
     return hipErrorInvalidValue;  // not reached: such passes hold at most four rows
   return hipGetLastError();
 }
 
+template <int FMT, int S, int RR, int W>
+hipError_t quads_dt(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx, float *y,
+                    int64_t ldy, int rq, int grid, hipStream_t st) {
+  if (xd == DT_F32) return quads_go<FMT, S, RR, W, DT_F32>(p, x, batch, ldx, y, ldy, rq, grid, st);
+  if (xd == DT_BF16) return quads_go<FMT, S, RR, W, DT_BF16>(p, x, batch, ldx, y, ldy, rq, grid, st);
+  return quads_go<FMT, S, RR, W, DT_F16>(p, x, batch, ldx, y, ldy, rq, grid, st);
+}
+
 template <int S, int RR, int W>
-hipError_t ptq1_dt(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx, float *y,
-                   int64_t ldy, int rq, int grid, hipStream_t st) {
-  if (xd == DT_F32) return ptq1_go<S, RR, W, DT_F32>(p, x, batch, ldx, y, ldy, rq, grid, st);
-  if (xd == DT_BF16) return ptq1_go<S, RR, W, DT_BF16>(p, x, batch, ldx, y, ldy, rq, grid, st);
-  return ptq1_go<S, RR, W, DT_F16>(p, x, batch, ldx, y, ldy, rq, grid, st);
+hipError_t quads_fmt(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx, float *y,
+                     int64_t ldy, int rq, int grid, hipStream_t st) {
+  if (p.fmt == FMT_PTQ1) return quads_dt<FMT_PTQ1, S, RR, W>(p, x, xd, batch, ldx, y, ldy, rq, grid, st);
+  return quads_dt<FMT_PQ2, S, RR, W>(p, x, xd, batch, ldx, y, ldy, rq, grid, st);
 }
 
 // Waves per workgroup (up to twelve, fewer for short rows: a wave covers 16
 // chunks a slot) and slots per lane for k/32 chunks.
-void ptq1_split(int chunks, int &W, int &S) {
+void quads_split(int chunks, int &W, int &S) {
   const int cw = (chunks + 15) / 16;
   W = cw <= 4 ? 4 : cw <= 8 ? 8 : 12;
   S = (chunks + 16 * W - 1) / (16 * W);
@@ -431,18 +478,18 @@ void ptq1_split(int chunks, int &W, int &S) {
 
 // Batch rows one pass can hold: eight where the activations of eight rows
 // fit the registers (up to three slots, 16-bit activations), else four.
-int ptq1_pass_rows(const Planes &p, int xd) {
+int quads_pass_rows(const Planes &p, int xd) {
   int W, S;
-  ptq1_split((int)(p.k / 32), W, S);
+  quads_split((int)(p.k / 32), W, S);
   return S <= 3 && xd != DT_F32 ? 8 : 4;
 }
 
-// One pass of up to ptq1_pass_rows batch rows.
-hipError_t ptq1_pass(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx, float *y,
+// One pass of up to quads_pass_rows batch rows.
+hipError_t quads_pass(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx, float *y,
                      int64_t ldy, hipStream_t st) {
   const int chunks = (int)(p.k / 32);
   int W, S;
-  ptq1_split(chunks, W, S);
+  quads_split(chunks, W, S);
   // row-quads per workgroup: an equal share per compute unit, at most RQMAX
   const int cus = device_cus();
   const int64_t nq = (p.n + 3) / 4;
@@ -451,36 +498,36 @@ hipError_t ptq1_pass(const Planes &p, const void *x, int xd, int64_t batch, int6
   const int64_t grid = (nq + rq - 1) / rq;
   // row-quads of loads in flight: S*RR steps (a last partial round skips
   // the row-quads past the workgroup's share)
-#define TQ_PTQ1_W(WW)                                                                         \
+#define TQ_QUADS_W(WW)                                                                         \
   switch (S) {                                                                                \
-    case 1: return ptq1_dt<1, 5, WW>(p, x, xd, batch, ldx, y, ldy, (int)rq, (int)grid, st);   \
-    case 2: return ptq1_dt<2, 3, WW>(p, x, xd, batch, ldx, y, ldy, (int)rq, (int)grid, st);   \
-    case 3: return ptq1_dt<3, 2, WW>(p, x, xd, batch, ldx, y, ldy, (int)rq, (int)grid, st);   \
-    default: return ptq1_dt<4, 1, WW>(p, x, xd, batch, ldx, y, ldy, (int)rq, (int)grid, st);  \
+    case 1: return quads_fmt<1, 5, WW>(p, x, xd, batch, ldx, y, ldy, (int)rq, (int)grid, st);   \
+    case 2: return quads_fmt<2, 3, WW>(p, x, xd, batch, ldx, y, ldy, (int)rq, (int)grid, st);   \
+    case 3: return quads_fmt<3, 2, WW>(p, x, xd, batch, ldx, y, ldy, (int)rq, (int)grid, st);   \
+    default: return quads_fmt<4, 1, WW>(p, x, xd, batch, ldx, y, ldy, (int)rq, (int)grid, st);  \
   }
   switch (W) {
-    case 4: TQ_PTQ1_W(4)
-    case 8: TQ_PTQ1_W(8)
-    default: TQ_PTQ1_W(12)
+    case 4: TQ_QUADS_W(4)
+    case 8: TQ_QUADS_W(8)
+    default: TQ_QUADS_W(12)
   }
-#undef TQ_PTQ1_W
+#undef TQ_QUADS_W
 }
 
 }  // namespace
 
 // k up to 12 waves x 4 slots x 16 chunks x 32 weights.
-bool gemv_ptq1_fits(const Planes &p) {
-  return p.fmt == FMT_PTQ1 && p.k % 128 == 0 && p.k / 32 <= 12 * 4 * 16 &&
+bool gemv_quads_fits(const Planes &p) {
+  return (p.fmt == FMT_PTQ1 || p.fmt == FMT_PQ2) && p.k % 128 == 0 && p.k / 32 <= 12 * 4 * 16 &&
          p.n * p.base_row < (int64_t(1) << 31);
 }
 
-hipError_t launch_gemv_ptq1(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx,
+hipError_t launch_gemv_quads(const Planes &p, const void *x, int xd, int64_t batch, int64_t ldx,
                             float *y, int64_t ldy, hipStream_t st) {
   const int64_t esz = xd == DT_F32 ? 4 : 2;
-  const int64_t step = ptq1_pass_rows(p, xd);
+  const int64_t step = quads_pass_rows(p, xd);
   for (int64_t b0 = 0; b0 < batch; b0 += step) {
     const int64_t nb = batch - b0 < step ? batch - b0 : step;
-    hipError_t e = ptq1_pass(p, static_cast<const char *>(x) + b0 * ldx * esz, xd, nb, ldx,
+    hipError_t e = quads_pass(p, static_cast<const char *>(x) + b0 * ldx * esz, xd, nb, ldx,
                              y + b0 * ldy, ldy, st);
     if (e != hipSuccess) return e;
   }

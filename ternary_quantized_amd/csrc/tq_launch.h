@@ -35,11 +35,11 @@ hipError_t launch_gemm(const Planes &p, const uint16_t *x, int x_dtype,
 
 int64_t gemv_max_k(int fmt);
 
-// PTQ1_0 GEMV on the matrix cores (any batch, in passes of four rows):
-// shapes it covers, and the launch.
-bool gemv_ptq1_fits(const Planes &p);
-hipError_t launch_gemv_ptq1(const Planes &p, const void *x, int x_dtype, int64_t batch,
-                            int64_t ldx, float *y, int64_t ldy, hipStream_t stream);
+// GEMV on the matrix cores over row-quads (either format, any batch, in
+// passes of up to eight rows): shapes it covers, and the launch.
+bool gemv_quads_fits(const Planes &p);
+hipError_t launch_gemv_quads(const Planes &p, const void *x, int x_dtype, int64_t batch,
+                             int64_t ldx, float *y, int64_t ldy, hipStream_t stream);
 
 // Signed transform fused into the GEMV (one launch): supported shapes, and
 // the launch itself (x unrotated, signs bf16 +-1; tiles > 0 gathers x into

@@ -129,19 +129,22 @@ def test_gemv_parity(fmt, n, k, batch):
     assert_within(to_f64(torch, y), expect, bound, "gemv")
 
 
+@pytest.mark.parametrize("fmt", ["PQ2_0_G128", "PTQ1_0_G128"])
 @pytest.mark.parametrize("k", [1024, 4096, 11264, 17408])
-@pytest.mark.parametrize("batch,xdt", [(5, "bf16"), (6, "f16"), (8, "bf16"), (7, "f16")])
-def test_gemv_ptq1_eight_row_passes(k, batch, xdt):
-    """PTQ1_0 with 16-bit activations and five to eight batch rows runs one
-    pass that decodes each weight once for two groups of four rows (every
-    wave count and slot count of the split, and partial second groups)."""
+@pytest.mark.parametrize("batch,xdt", [(2, "f16"), (5, "bf16"), (6, "f16"), (8, "bf16"), (7, "f16"),
+                                       (8, "f32")])
+def test_gemv_row_quads_batches(fmt, k, batch, xdt):
+    """The row-quad MFMA GEMV at two to eight batch rows: with 16-bit
+    activations five to eight rows run in one pass that decodes each weight
+    once for two groups of four rows (every wave count and slot count of the
+    split, partial second groups); fp32 activations run passes of four."""
     n = 1000 if k < 17408 else 333
-    payload, xr = gemv_case("PTQ1_0_G128", n, k, batch, xdt, seed=k + batch)
-    say("gemv ptq1 eight-row pass n=%d k=%d batch=%d x=%s" % (n, k, batch, xdt))
-    y = tq.gemv_rowsplit(dev(torch, payload), "PTQ1_0_G128", n, k, x_dev(torch, xr, xdt))
+    payload, xr = gemv_case(fmt, n, k, batch, xdt, seed=k + batch)
+    say("gemv row quads %s n=%d k=%d batch=%d x=%s" % (fmt, n, k, batch, xdt))
+    y = tq.gemv_rowsplit(dev(torch, payload), fmt, n, k, x_dev(torch, xr, xdt))
     torch.cuda.synchronize()
-    expect, bound = P.project_payload("PTQ1_0_G128", n, k, payload, x_f64(xr, xdt))
-    assert_within(to_f64(torch, y), expect, bound, "gemv ptq1 eight rows")
+    expect, bound = P.project_payload(fmt, n, k, payload, x_f64(xr, xdt))
+    assert_within(to_f64(torch, y), expect, bound, "gemv row quads")
 
 
 # ------------------------------------------- fused transform + GEMV ---
