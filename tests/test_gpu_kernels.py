@@ -147,6 +147,23 @@ def test_gemv_row_quads_batches(fmt, k, batch, xdt):
     assert_within(to_f64(torch, y), expect, bound, "gemv row quads")
 
 
+@pytest.mark.parametrize("fmt,k", [("PQ2_0_G128", 65536), ("PQ2_0_G128", 25600), ("PTQ1_0_G128", 32768),
+                                   ("PTQ1_0_G128", 24576)])
+@pytest.mark.parametrize("batch", [1, 2, 5, 8])
+def test_gemv_longest_rows(fmt, k, batch):
+    """The longest rows the GEMV accepts (k = 65536 for PQ2_0, 32768 for
+    PTQ1_0) and the first rows past the row-quad kernel's reach, where the
+    lane-team kernels take over."""
+    n = 37
+    xdt = ["f32", "bf16", "f16"][batch % 3]
+    payload, xr = gemv_case(fmt, n, k, batch, xdt, seed=k + batch)
+    say("gemv longest rows %s n=%d k=%d batch=%d x=%s" % (fmt, n, k, batch, xdt))
+    y = tq.gemv_rowsplit(dev(torch, payload), fmt, n, k, x_dev(torch, xr, xdt))
+    torch.cuda.synchronize()
+    expect, bound = P.project_payload(fmt, n, k, payload, x_f64(xr, xdt))
+    assert_within(to_f64(torch, y), expect, bound, "gemv longest rows")
+
+
 # ------------------------------------------- fused transform + GEMV ---
 @pytest.mark.parametrize("n,k", [(1, 1024), (77, 3072), (1000, 5120), (300, 11264)])
 @pytest.mark.parametrize("xdt", ["f32", "bf16", "f16"])
