@@ -16,7 +16,10 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 SHAPES = [("PQ2_0_G128", 3, 200), ("PTQ1_0_G128", 3, 200), ("PQ2_0_G128", 7, 1024),
-          ("PTQ1_0_G128", 1000, 5120), ("PQ2_0_G128", 17408, 5120), ("PTQ1_0_G128", 5120, 17408)]
+          ("PTQ1_0_G128", 1000, 5120), ("PQ2_0_G128", 17408, 5120), ("PTQ1_0_G128", 5120, 17408),
+          # odd block counts (PQ2_0 blocks move in pairs, the last one alone)
+          ("PQ2_0_G128", 1, 128), ("PQ2_0_G128", 3, 384), ("PQ2_0_G128", 1001, 640),
+          ("PTQ1_0_G128", 1, 128)]
 
 
 @pytest.mark.parametrize("fmt,n,k", SHAPES)
