@@ -431,6 +431,14 @@ def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream):
         wd = torch.randn((n5, k5), device=x5.device, dtype=torch.float16).t().contiguous()
         tmean = event_timed(torch, lambda i: torch.matmul(xr5, wd), 10)
         del wd
+        # the same shape with the weights as PTQ1_0 planes
+        p5t = to_dev(tq.pack_rowsplit("PTQ1_0_G128", c5["trits"], c5["scale_bits"]))
+        pmean = event_timed(torch, lambda i: tq.gemm_rowsplit(p5t, "PTQ1_0_G128", n5, k5, xr5,
+                                                                  out=y5), 10)
+        del p5t
+        res["cfg5_shape_ptq1_gemm"] = {"mean_launch_us": round(pmean * 1e6, 2),
+                                       "tflops": round(flops / pmean / 1e12, 1),
+                                       "mfma_frac": round(flops / pmean / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
         res["cfg5_prefill_gemm"] = {"m": int(x5.shape[0]), "n": n5, "k": k5,
                                     "mean_launch_us": round(gmean * 1e6, 2),
                                     "tflops": round(flops / gmean / 1e12, 1),

@@ -4,18 +4,13 @@
 // §4.4 (every low-bit projection multiplies the rotated activations).
 //
 // This is a genuinely dense contraction, so it runs on the matrix cores
-// (v_mfma_f32_32x32x16_f16, fp32 accumulation).  Each K step is one
-// 128-weight group: the workgroup stages its X tile in LDS as binary16 and
-// decodes its weight tile into LDS as the binary16 values t*s.  That value is
-// exact -- s is itself a binary16 and t is -1, 0 or +1 -- so folding the
-// group scale into the decoded weight loses nothing, and the only rounding
-// before the fp32 accumulation is that of X to binary16.
-//
-// Workgroup: 256 threads (4 waves in a 2x2 arrangement), a 128x128 output
-// tile, each wave a 64x64 sub-tile of 2x2 MFMA blocks of 32x32.
-// Workgroups are numbered N-tile-major inside each M-tile band and the band
-// is chosen from the XCD the workgroup lands on (workgroups are dealt to the
-// 8 XCDs round-robin), so the workgroups that share an X tile share an L2.
+// (v_mfma_f32_32x32x16_f16, fp32 accumulation).  The workgroup stages its X
+// tile in LDS as binary16 and decodes its weight tile into LDS as the
+// binary16 values t*s.  That value is exact -- s is itself a binary16 and t
+// is -1, 0 or +1 -- so folding the group scale into the decoded weight loses
+// nothing, and the only rounding before the fp32 accumulation is that of X
+// to binary16.  Output tiles are dealt XCD-aware: the workgroups of one XCD
+// walk one M band, so that band's X stays in that XCD's L2.
 
 #include "tq_device.h"
 #include "tq_launch.h"
@@ -25,212 +20,11 @@ namespace tq {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int GM = 128, GN = 128, GK = 128;
-constexpr int LDSROW = GK + 8;  // halves per LDS row (16-byte pad)
-
-__device__ __forceinline__ half2_t cvt_pair(uint32_t v, int sel) {
-  switch (sel) {
-    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0);
-    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1);
-    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2);
-    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3);
-  }
-}
-
-__device__ __forceinline__ uint32_t h2_bits(half2_t h) {
-  uint32_t u;
-  __builtin_memcpy(&u, &h, 4);
-  return u;
-}
-
-// fp4 pair (u/2, v/2) -> (u-1)*s, (v-1)*s exactly: fma(c/2, 2s, -s).
-__device__ __forceinline__ uint32_t scale_pair(half2_t c_half, half2_t s2, half2_t neg_s) {
-  return h2_bits(__builtin_elementwise_fma(c_half, s2, neg_s));
-}
-
-// PQ2_0: one dword = 16 codes (weights 16d..16d+15, LSB pair first) ->
-// 8 binary16 pairs in natural order, each value (code-1)*s.
-__device__ __forceinline__ void decode_pq2_dword(uint32_t d, half2_t s2, half2_t ns,
-                                                 uint32_t out[8]) {
-  // byte q of p01 holds codes 4q (low nibble) and 4q+1 (high nibble);
-  // byte q of p23 holds codes 4q+2 and 4q+3.
-  const uint32_t p01 = (d & 0x03030303u) | ((d << 2) & 0x30303030u);
-  const uint32_t p23 = ((d >> 4) & 0x03030303u) | ((d >> 2) & 0x30303030u);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    out[2 * q] = scale_pair(cvt_pair(p01, q), s2, ns);
-    out[2 * q + 1] = scale_pair(cvt_pair(p23, q), s2, ns);
-  }
-}
-
-// PTQ1_0: trits 5b..5b+4 of a base byte v (digit i = v/3^i mod 3).
-__device__ __forceinline__ void ptq1_digits(uint32_t v, int n, uint32_t *d) {
-  for (int i = 0; i < n; ++i) { d[i] = v % 3u; v /= 3u; }
-}
-
-template <int FMT, int XD, int YD>
-__global__ __launch_bounds__(256) void gemm_kernel(Planes p, const uint16_t *__restrict__ X,
-                                                   int64_t M, int64_t ldx, void *__restrict__ Y,
-                                                   int64_t ldy, int tiles_n, int tiles_m) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[GM * LDSROW];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[GN * LDSROW];
-
-  // XCD-aware tile order: workgroup b runs on XCD b % 8; consecutive slots
-  // on one XCD walk the N tiles of one M band.
-  const int nwg = tiles_n * tiles_m;
-  const int b = blockIdx.x;
-  int tile;
-  if (nwg % 8 == 0) {
-    const int per_xcd = nwg / 8;
-    tile = (b % 8) * per_xcd + b / 8;
-  } else {
-    tile = b;
-  }
-  const int tm = tile / tiles_n, tn = tile % tiles_n;
-  const int64_t m0 = (int64_t)tm * GM, n0 = (int64_t)tn * GN;
-
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-
-  floatx16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  for (int64_t g = 0; g < p.groups; ++g) {
-    __syncthreads();
-    // ---- stage X[m0:m0+128][128g:128g+128] as binary16
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = t + 256 * i;
-      const int r = idx >> 4, c8 = (idx & 15) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m0 + r < M) {
-        v = *reinterpret_cast<const uint4 *>(X + (m0 + r) * ldx + g * GK + c8);
-        if constexpr (XD == DT_BF16) {
-          uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = f32_to_f16(bf16_to_f32((uint16_t)(w[e] & 0xFFFF)));
-            const uint32_t hi = f32_to_f16(bf16_to_f32((uint16_t)(w[e] >> 16)));
-            w[e] = lo | (hi << 16);
-          }
-          v = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-      }
-      *reinterpret_cast<uint4 *>(&As[r * LDSROW + c8]) = v;
-    }
-    // ---- decode W[n0:n0+128][group g] into t*s binary16
-    if constexpr (FMT == FMT_PQ2) {
-      const int r = t >> 1, half = t & 1;  // 64 weights per thread
-      uint32_t o[32];
-      if (n0 + r < p.n) {
-        const int64_t row = n0 + r;
-        const uint4 q = *reinterpret_cast<const uint4 *>(p.base + row * p.base_row + g * 32 +
-                                                          16 * half);
-        const _Float16 s = (_Float16)f16_to_f32(p.scale[row * p.groups + g]);
-        half2_t s2, ns;
-        s2.x = s2.y = (_Float16)(2.0f * (float)s);
-        ns.x = ns.y = -s;
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int d = 0; d < 4; ++d) decode_pq2_dword(w[d], s2, ns, o + 8 * d);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) o[i] = 0;
-      }
-      uint4 *dst = reinterpret_cast<uint4 *>(&Bs[r * LDSROW + 64 * half]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
-    } else {
-      // two quarter-groups (32 trits) per thread
-#pragma unroll
-      for (int rep = 0; rep < 2; ++rep) {
-        const int qi = t + 256 * rep;  // 0..511
-        const int r = qi >> 2, q = qi & 3;
-        _Float16 vals[32];
-        if (n0 + r < p.n) {
-          const int64_t row = n0 + r;
-          const uint8_t *bb = p.base + row * p.base_row + g * 24;
-          const uint8_t *hb = p.high + row * p.high_row + g * 2;
-          const _Float16 s = (_Float16)f16_to_f32(p.scale[row * p.groups + g]);
-          const _Float16 zero = (_Float16)0.0f;
-          // trits 30q..30q+29 from base bytes 6q..6q+5, then 120+2q, 121+2q
-#pragma unroll
-          for (int by = 0; by < 6; ++by) {
-            uint32_t d[5];
-            ptq1_digits(bb[6 * q + by], 5, d);
-#pragma unroll
-            for (int e = 0; e < 5; ++e)
-              vals[5 * by + e] = d[e] == 0 ? -s : (d[e] == 1 ? zero : (d[e] == 2 ? s : (_Float16)(2.0f * (float)s)));
-          }
-          uint32_t dh[4];
-          ptq1_digits(hb[q >> 1], 4, dh);
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const uint32_t dd = dh[2 * (q & 1) + e];
-            vals[30 + e] = dd == 0 ? -s : (dd == 1 ? zero : s);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 32; ++i) vals[i] = (_Float16)0.0f;
-        }
-        // natural k order inside the group: trits 30q.. and 120+2q..
-        _Float16 *dst = &Bs[r * LDSROW];
-#pragma unroll
-        for (int e = 0; e < 30; ++e) dst[30 * q + e] = vals[e];
-        dst[120 + 2 * q] = vals[30];
-        dst[121 + 2 * q] = vals[31];
-      }
-    }
-    __syncthreads();
-
-    // ---- 8 k-steps of 16 on the matrix cores
-#pragma unroll
-    for (int ks = 0; ks < GK / 16; ++ks) {
-      half8_t a[2], bfr[2];
-      const int kb = ks * 16 + 8 * (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const half8_t *>(&As[(wm + 32 * i + (lane & 31)) * LDSROW + kb]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = *reinterpret_cast<const half8_t *>(&Bs[(wn + 32 * j + (lane & 31)) * LDSROW + kb]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  }
-
-  // ---- epilogue: D[i][j] of a 32x32 block sits in lane (j + 32*(i/4 % 2)),
-  // value (i/8)*4 + i%4
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + wn + 32 * j + (lane & 31);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < M && col < p.n) {
-          if constexpr (YD == DT_F32)
-            static_cast<float *>(Y)[row * ldy + col] = acc[i][j][v];
-          else
-            static_cast<uint16_t *>(Y)[row * ldy + col] = f32_to_bf16(acc[i][j][v]);
-        }
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// PQ2_0 prefill GEMM: 512-thread workgroups (8 waves), 64-deep K steps
-// through two LDS stages, one barrier per step.
+// Pipelined prefill GEMM: 512-thread workgroups (8 waves), 64-deep K steps
+// through two LDS stages, one barrier per step.  PQ2_0 planes hold the 2-bit
+// codes; PTQ1_0 planes are turned into the same 2-bit code words on the way
+// in (below), so both formats share the decode and everything after it.
 //
 // Stage layout: X rows and decoded weight rows of [64 k + 8 pad] binary16.
 // Inside every 16-wide k block both are stored in the k order
@@ -251,7 +45,50 @@ __global__ __launch_bounds__(256) void gemm_kernel(Planes p, const uint16_t *__r
 // 64) for the bulk, and 128 x 64 sub-tiles (waves 4 x 2 of 32 x 32) for the
 // tiles of a last, partial round, which is split 8 ways so it fills the
 // chip instead of a fraction of it.
+//
+// PTQ1_0: a K step covers half a group, and a weight thread's 32 weights
+// are one 64-bit word of the group's 2-bit code string (code = radix-3
+// digit = trit + 1, weight j at bits 2j): word w = 2*(step & 1) + half.  A
+// 256-entry LDS table gives a byte's five digits as a 10-bit field, and the
+// word is assembled from the fields of the base bytes (and high bytes) it
+// overlaps, each at a fixed shift.  The thread loads the 12 base bytes that
+// hold them (bytes 0-11, 4-15, 12-23, 12-23 for words 0-3) and the group's two
+// high bytes.  The half is chosen per wave, so the word is uniform in a wave.
 constexpr int G2K = 64, G2ROW = G2K + 8;
+
+// Word w of a PTQ1_0 group's code string from its base window b[3] (bytes
+// 0-11, 4-15 or 12-23 of the group for w = 0, 1, 2-3) and high bytes h.
+__device__ __forceinline__ uint64_t ptq1_code_word(const uint32_t (&b)[3], uint32_t h, int w,
+                                                   const uint16_t *lut) {
+  auto byte = [&](int i) -> uint32_t { return (b[i >> 2] >> (8 * (i & 3))) & 0xFFu; };
+  auto field = [&](int i) -> uint64_t { return lut[byte(i)]; };
+  uint64_t acc = 0;
+  // field of group byte j sits at bit 10j - 64w of the word
+  switch (w) {
+    case 0:  // group bytes 0..6 = window bytes 0..6
+#pragma unroll
+      for (int j = 0; j <= 6; ++j) acc |= field(j) << (10 * j);
+      break;
+    case 1:  // group bytes 6..12 = window bytes 2..8
+      acc = field(2) >> 4;
+#pragma unroll
+      for (int j = 7; j <= 12; ++j) acc |= field(j - 4) << (10 * j - 64);
+      break;
+    case 2:  // group bytes 12..19 = window bytes 0..7
+      acc = field(0) >> 8;
+#pragma unroll
+      for (int j = 13; j <= 19; ++j) acc |= field(j - 12) << (10 * j - 128);
+      break;
+    default:  // group bytes 19..23 = window bytes 7..11, then the high bytes
+      acc = field(7) >> 2;
+#pragma unroll
+      for (int j = 20; j <= 23; ++j) acc |= field(j - 12) << (10 * j - 192);
+      acc |= (uint64_t)(lut[h & 0xFFu] & 0xFFu) << 48;
+      acc |= (uint64_t)(lut[(h >> 8) & 0xFFu] & 0xFFu) << 56;
+      break;
+  }
+  return acc;
+}
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -296,11 +133,11 @@ __device__ __forceinline__ uint32_t x_pair_f16(uint32_t v) {
 
 // One output tile of TM x TN at (m0, n0): waves WAVES_M x (8 / WAVES_M),
 // each 32*FM x 32*FN.
-template <int XD, int YD, int TM, int TN, int FM, int FN, int WAVES_M>
-__device__ __forceinline__ void gemm_pq2_tile(const Planes &p, const uint16_t *__restrict__ X,
+template <int FMT, int XD, int YD, int TM, int TN, int FM, int FN, int WAVES_M>
+__device__ __forceinline__ void gemm_planes_tile(const Planes &p, const uint16_t *__restrict__ X,
                                               int64_t M, int64_t ldx, void *__restrict__ Y,
                                               int64_t ldy, int64_t m0, int64_t n0,
-                                              _Float16 *lds2) {
+                                              _Float16 *lds2, const uint16_t *lut) {
   constexpr int WAVES_N = 8 / WAVES_M;
   static_assert(WAVES_M * 32 * FM == TM && WAVES_N * 32 * FN == TN, "wave grid must cover the tile");
   constexpr int TPR = 512 / TM;       // threads per X row
@@ -323,13 +160,18 @@ __device__ __forceinline__ void gemm_pq2_tile(const Planes &p, const uint16_t *_
   // compiler keeps counting the loads in flight instead of waiting for all
   // of them where a branch around a load would rejoin)
   const bool wthread = 2 * TN >= 512 || t < 2 * TN;
-  const int wr = wthread ? t >> 1 : 0, wh = t & 1;
+  // PQ2_0: neighbouring lanes take the two halves of a row; PTQ1_0: the half
+  // is the wave's (its code word must be uniform in a wave)
+  const int wr = !wthread ? 0 : FMT == FMT_PQ2 ? t >> 1 : (((t >> 7) << 6) | (t & 63));
+  const int wh = FMT == FMT_PQ2 ? (t & 1) : __builtin_amdgcn_readfirstlane((t >> 6) & 1);
   const bool wrow_ok = wthread && n0 + wr < p.n;
   const int64_t wrow = wrow_ok ? n0 + wr : 0;
-  const uint8_t *wsrc = p.base + wrow * p.base_row + 8 * wh;
+  const uint8_t *wsrc = p.base + wrow * p.base_row + (FMT == FMT_PQ2 ? 8 * wh : 0);
+  const uint16_t *hsrc = reinterpret_cast<const uint16_t *>(p.high + wrow * p.high_row);
   const uint16_t *ssrc = p.scale + wrow * p.groups;
 
-  uint32_t xreg[2][HX / 2], wreg[4][2], sreg[4];
+  constexpr int WW = FMT == FMT_PQ2 ? 2 : 3;  // code (PQ2_0) or base (PTQ1_0) dwords per step
+  uint32_t xreg[2][HX / 2], wreg[4][WW], hreg[4], sreg[4];
   auto clamp = [&](int st) { return st < nsteps ? st : nsteps - 1; };  // past the end: a harmless re-read
   auto load_x = [&](int set, int st) {
     const int64_t k0 = (int64_t)clamp(st) * G2K;
@@ -344,17 +186,31 @@ __device__ __forceinline__ void gemm_pq2_tile(const Planes &p, const uint16_t *_
   auto load_w = [&](int set, int st) {
     if (wthread) {
       const int64_t k0 = (int64_t)clamp(st) * G2K;
-      const u32x2_t w = *reinterpret_cast<const u32x2_t *>(wsrc + k0 / 4);
-      wreg[set][0] = w[0];
-      wreg[set][1] = w[1];
+      if constexpr (FMT == FMT_PQ2) {
+        const u32x2_t w = *reinterpret_cast<const u32x2_t *>(wsrc + k0 / 4);
+        wreg[set][0] = w[0];
+        wreg[set][1] = w[1];
+      } else {
+        // group k0/128, window at byte 0, 4 or 12 of its 24 base bytes
+        const int word = 2 * (clamp(st) & 1) + wh;
+        const int off = word == 0 ? 0 : word == 1 ? 4 : 12;
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(wsrc + (k0 / 128) * 24 + off);
+        wreg[set][0] = w[0];
+        wreg[set][1] = w[1];
+        wreg[set][2] = w[2];
+        hreg[set] = hsrc[k0 / 128];
+      }
       sreg[set] = ssrc[k0 / 128];
     }
   };
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(magic));
+  // PTQ1_0: the code word of code set `wset` (built at q = 0, used by q = 0..3)
+  uint32_t cw[2] = {0u, 0u};
   // quarter q of X set `set` and code set `wset` into an LDS stage: one
-  // 16-byte write of permuted X (while q < XQ) and one of 8 decoded weights
-  auto store_piece = [&](int set, int wset, int buf, int q) {
+  // 16-byte write of permuted X (while q < XQ) and one of 8 decoded weights;
+  // par = parity of the step being stored
+  auto store_piece = [&](int set, int wset, int buf, int q, int par) {
     _Float16 *As = lds2 + buf * STAGE;
     _Float16 *Bs = As + TM * G2ROW;
     if (q < XQ) {
@@ -377,10 +233,21 @@ __device__ __forceinline__ void gemm_pq2_tile(const Planes &p, const uint16_t *_
       half2_t s2;
       s2.x = s2.y = wrow_ok ? sh : (_Float16)0.0f;
       uint32_t o[4];
+      uint32_t d;
+      if constexpr (FMT == FMT_PQ2) {
+        d = wreg[wset][q >> 1];
+      } else {
+        if (q == 0) {
+          const uint64_t c = ptq1_code_word(wreg[wset], hreg[wset], 2 * par + wh, lut);
+          cw[0] = (uint32_t)c;
+          cw[1] = (uint32_t)(c >> 32);
+        }
+        d = cw[q >> 1];
+      }
       if (q & 1)
-        decode_pq2_ts4<1>(wreg[wset][q >> 1], magic, s2, o);
+        decode_pq2_ts4<1>(d, magic, s2, o);
       else
-        decode_pq2_ts4<0>(wreg[wset][q >> 1], magic, s2, o);
+        decode_pq2_ts4<0>(d, magic, s2, o);
       *reinterpret_cast<u32x4_t *>(Bs + wr * G2ROW + 32 * wh + 8 * q) =
           (u32x4_t){o[0], o[1], o[2], o[3]};
     }
@@ -426,7 +293,7 @@ __device__ __forceinline__ void gemm_pq2_tile(const Planes &p, const uint16_t *_
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks & 1][i], bf[ks & 1][j], acc[i][j],
                                                              0, 0, 0);
-      store_piece((ph + 1) & 1, (ph + 1) & 3, buf ^ 1, ks);
+      store_piece((ph + 1) & 1, (ph + 1) & 3, buf ^ 1, ks, (ph + 1) & 1);
     }
     __syncthreads();
   };
@@ -437,7 +304,7 @@ __device__ __forceinline__ void gemm_pq2_tile(const Planes &p, const uint16_t *_
 #pragma unroll
   for (int i = 1; i < 4; ++i) load_w(i, i);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) store_piece(0, 0, 0, q);
+  for (int q = 0; q < 4; ++q) store_piece(0, 0, 0, q, 0);
   __syncthreads();
   for (int s = 0; s < nsteps; s += 4) {  // nsteps is even
     step(s, 0);
@@ -483,12 +350,27 @@ struct GemmSplit {
   int xcd;
 };
 
-template <int XD, int YD>
-__global__ __launch_bounds__(512) void gemm_pq2_kernel(Planes p, const uint16_t *__restrict__ X,
+template <int FMT, int XD, int YD>
+__global__ __launch_bounds__(512) void gemm_planes_kernel(Planes p, const uint16_t *__restrict__ X,
                                                        int64_t M, int64_t ldx,
                                                        void *__restrict__ Y, int64_t ldy,
                                                        GemmSplit sp) {
   extern __shared__ __attribute__((aligned(16))) _Float16 lds2[];
+  // PTQ1_0: digit i of byte v as the 2-bit field i (the first stage's
+  // barrier orders these writes before any use)
+  __shared__ uint16_t lut[FMT == FMT_PTQ1 ? 256 : 1];
+  if constexpr (FMT == FMT_PTQ1) {
+    if (threadIdx.x < 256) {
+      uint32_t v = threadIdx.x, f = 0;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        f |= (v % 3u) << (2 * i);
+        v /= 3u;
+      }
+      lut[threadIdx.x] = (uint16_t)f;
+    }
+    __syncthreads();
+  }
   const int b = blockIdx.x;
   int tile, sub = -1;
   if (b < sp.nbig) {
@@ -506,14 +388,14 @@ __global__ __launch_bounds__(512) void gemm_pq2_kernel(Planes p, const uint16_t 
   }
   const int64_t m0 = (int64_t)(tile / sp.tiles_n) * 256, n0 = (int64_t)(tile % sp.tiles_n) * 256;
   if (sub < 0)
-    gemm_pq2_tile<XD, YD, 256, 256, 4, 2, 2>(p, X, M, ldx, Y, ldy, m0, n0, lds2);
+    gemm_planes_tile<FMT, XD, YD, 256, 256, 4, 2, 2>(p, X, M, ldx, Y, ldy, m0, n0, lds2, lut);
   else
-    gemm_pq2_tile<XD, YD, 128, 64, 1, 1, 4>(p, X, M, ldx, Y, ldy, m0 + 128 * (sub >> 2),
-                                            n0 + 64 * (sub & 3), lds2);
+    gemm_planes_tile<FMT, XD, YD, 128, 64, 1, 1, 4>(p, X, M, ldx, Y, ldy, m0 + 128 * (sub >> 2),
+                                                 n0 + 64 * (sub & 3), lds2, lut);
 }
 
-template <int XD, int YD>
-static hipError_t gemm_pq2_go(const Planes &p, const uint16_t *x, int64_t m, int64_t ldx, void *y,
+template <int FMT, int XD, int YD>
+static hipError_t gemm_planes_go(const Planes &p, const uint16_t *x, int64_t m, int64_t ldx, void *y,
                               int64_t ldy, hipStream_t st) {
   GemmSplit sp;
   sp.tiles_n = (int)((p.n + 255) / 256);
@@ -533,7 +415,7 @@ static hipError_t gemm_pq2_go(const Planes &p, const uint16_t *x, int64_t m, int
   }
   const int grid = sp.nbig + 8 * (total - sp.nbig);
   const size_t lds = (size_t)2 * (256 + 256) * G2ROW * sizeof(_Float16);
-  auto kern = gemm_pq2_kernel<XD, YD>;
+  auto kern = gemm_planes_kernel<FMT, XD, YD>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -541,36 +423,21 @@ static hipError_t gemm_pq2_go(const Planes &p, const uint16_t *x, int64_t m, int
   return hipGetLastError();
 }
 
-template <int FMT, int XD>
-static hipError_t gemm_go(const Planes &p, const uint16_t *x, int64_t m, int64_t ldx, void *y,
-                          int yd, int64_t ldy, hipStream_t st) {
-  const int tiles_n = (int)((p.n + GN - 1) / GN);
-  const int tiles_m = (int)((m + GM - 1) / GM);
-  dim3 grid((unsigned)(tiles_n * tiles_m)), block(256);
-  if (yd == DT_F32)
-    hipLaunchKernelGGL((gemm_kernel<FMT, XD, DT_F32>), grid, block, 0, st, p, x, m, ldx, y, ldy,
-                       tiles_n, tiles_m);
-  else
-    hipLaunchKernelGGL((gemm_kernel<FMT, XD, DT_BF16>), grid, block, 0, st, p, x, m, ldx, y, ldy,
-                       tiles_n, tiles_m);
-  return hipGetLastError();
-}
-
 hipError_t launch_gemm(const Planes &p, const uint16_t *x, int xd, int64_t m, int64_t ldx, void *y,
                        int yd, int64_t ldy, hipStream_t st) {
-  // PQ2_0 with k a multiple of the 64-deep step: the pipelined 256x256 kernel
-  if (p.fmt == FMT_PQ2 && p.k % G2K == 0) {
+  // k is a multiple of 128 (checked by the entry point): whole 64-deep steps
+  if (p.fmt == FMT_PQ2) {
     if (xd == DT_F16)
-      return yd == DT_F32 ? gemm_pq2_go<DT_F16, DT_F32>(p, x, m, ldx, y, ldy, st)
-                          : gemm_pq2_go<DT_F16, DT_BF16>(p, x, m, ldx, y, ldy, st);
-    return yd == DT_F32 ? gemm_pq2_go<DT_BF16, DT_F32>(p, x, m, ldx, y, ldy, st)
-                        : gemm_pq2_go<DT_BF16, DT_BF16>(p, x, m, ldx, y, ldy, st);
+      return yd == DT_F32 ? gemm_planes_go<FMT_PQ2, DT_F16, DT_F32>(p, x, m, ldx, y, ldy, st)
+                          : gemm_planes_go<FMT_PQ2, DT_F16, DT_BF16>(p, x, m, ldx, y, ldy, st);
+    return yd == DT_F32 ? gemm_planes_go<FMT_PQ2, DT_BF16, DT_F32>(p, x, m, ldx, y, ldy, st)
+                        : gemm_planes_go<FMT_PQ2, DT_BF16, DT_BF16>(p, x, m, ldx, y, ldy, st);
   }
-  if (p.fmt == FMT_PQ2)
-    return xd == DT_F16 ? gemm_go<FMT_PQ2, DT_F16>(p, x, m, ldx, y, yd, ldy, st)
-                        : gemm_go<FMT_PQ2, DT_BF16>(p, x, m, ldx, y, yd, ldy, st);
-  return xd == DT_F16 ? gemm_go<FMT_PTQ1, DT_F16>(p, x, m, ldx, y, yd, ldy, st)
-                      : gemm_go<FMT_PTQ1, DT_BF16>(p, x, m, ldx, y, yd, ldy, st);
+  if (xd == DT_F16)
+    return yd == DT_F32 ? gemm_planes_go<FMT_PTQ1, DT_F16, DT_F32>(p, x, m, ldx, y, ldy, st)
+                        : gemm_planes_go<FMT_PTQ1, DT_F16, DT_BF16>(p, x, m, ldx, y, ldy, st);
+  return yd == DT_F32 ? gemm_planes_go<FMT_PTQ1, DT_BF16, DT_F32>(p, x, m, ldx, y, ldy, st)
+                      : gemm_planes_go<FMT_PTQ1, DT_BF16, DT_BF16>(p, x, m, ldx, y, ldy, st);
 }
 
 }  // namespace tq

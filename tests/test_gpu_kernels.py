@@ -288,17 +288,18 @@ def test_gemm_parity(fmt, m, n, k, xdt, ydt):
     assert_within(to_f64(torch, y), expect, bound, "gemm")
 
 
-def test_gemm_integer_exact_and_matches_gemv():
+@pytest.mark.parametrize("fmt", ["PQ2_0_G128", "PTQ1_0_G128"])
+def test_gemm_integer_exact_and_matches_gemv(fmt):
     rng = np.random.default_rng(4)
     m, n, k = 96, 320, 2048
     trits = synth.trits_uniform(rng, n, k)
     sb = np.full((n, k // 128), 0x3C00, np.uint16)
-    payload = dev(torch, tq.pack_rowsplit("PQ2_0_G128", trits, sb))
+    payload = dev(torch, tq.pack_rowsplit(fmt, trits, sb))
     xi = rng.integers(-8, 9, size=(m, k)).astype(np.float16)
     xd = dev(torch, xi.view(np.uint16).view(np.int16)).view(torch.float16)
-    y = tq.gemm_rowsplit(payload, "PQ2_0_G128", n, k, xd)
-    y2 = tq.gemm_rowsplit(payload, "PQ2_0_G128", n, k, xd)
-    yv = tq.gemv_rowsplit(payload, "PQ2_0_G128", n, k, xd[:8].contiguous())
+    y = tq.gemm_rowsplit(payload, fmt, n, k, xd)
+    y2 = tq.gemm_rowsplit(payload, fmt, n, k, xd)
+    yv = tq.gemv_rowsplit(payload, fmt, n, k, xd[:8].contiguous())
     torch.cuda.synchronize()
     expect = xi.astype(np.int64) @ trits.T.astype(np.int64)
     assert np.array_equal(y.cpu().numpy(), expect.astype(np.float32))
@@ -310,8 +311,9 @@ def _cus():
     return torch.cuda.get_device_properties(0).multi_processor_count
 
 
+@pytest.mark.parametrize("fmt", ["PQ2_0_G128", "PTQ1_0_G128"])
 @pytest.mark.parametrize("case", ["xcd_split", "plain_split", "two_steps"])
-def test_gemm_tail_split_integer_exact(case):
+def test_gemm_tail_split_integer_exact(case, fmt):
     """Tile counts just past a whole round of the device: the left-over
     256 x 256 tiles run as 128 x 64 sub-tiles.  Integer data make every
     output exact, so any tile or sub-tile mapping slip shows."""
@@ -331,11 +333,11 @@ def test_gemm_tail_split_integer_exact(case):
     rng = np.random.default_rng(len(case))
     trits = synth.trits_uniform(rng, n, k)
     sb = np.full((n, k // 128), 0x3C00, np.uint16)
-    payload = dev(torch, tq.pack_rowsplit("PQ2_0_G128", trits, sb))
+    payload = dev(torch, tq.pack_rowsplit(fmt, trits, sb))
     xi = rng.integers(-8, 9, size=(m, k)).astype(np.float16)
     xd = dev(torch, xi.view(np.uint16).view(np.int16)).view(torch.float16)
-    say("gemm tail split %s m=%d n=%d k=%d cus=%d" % (case, m, n, k, cus))
-    y = tq.gemm_rowsplit(payload, "PQ2_0_G128", n, k, xd)
+    say("gemm tail split %s %s m=%d n=%d k=%d cus=%d" % (fmt, case, m, n, k, cus))
+    y = tq.gemm_rowsplit(payload, fmt, n, k, xd)
     torch.cuda.synchronize()
     expect = xi.astype(np.float64) @ trits.T.astype(np.float64)  # exact: |sum| <= 2048
     got = y.cpu().numpy()
