@@ -519,10 +519,11 @@ static hipError_t gemv_wave_dt(const Planes &p, const void *x, int xd, const uin
   return gemv_wave_go<LAY_PLANES, A, BQ, DT_F16, FUSED>(p, x, signs, y, st, sa);
 }
 
-// k = 1024*m with m <= 11: pieces A = m/4 kilobytes + BQ = m%4 blocks.
-static bool gemv_wave_fits(const Planes &p) {
-  return p.fmt == FMT_PQ2 && p.k % 1024 == 0 && p.k / 1024 >= 1 && p.k / 1024 <= 11 &&
-         p.n < (int64_t(1) << 30);
+// k = 1024*m: pieces A = m/4 kilobytes + BQ = m%4 blocks; m <= 17 for the
+// GEMV alone, m <= 11 with the transform fused in.
+static bool gemv_wave_fits(const Planes &p, bool fused) {
+  return p.fmt == FMT_PQ2 && p.k % 1024 == 0 && p.k / 1024 >= 1 &&
+         p.k / 1024 <= (fused ? 11 : 17) && p.n < (int64_t(1) << 30);
 }
 
 template <bool FUSED>
@@ -539,8 +540,20 @@ static hipError_t gemv_wave(const Planes &p, const void *x, int xd, const uint16
     case 8: return gemv_wave_dt<2, 0, FUSED>(p, x, xd, signs, y, st, sa);
     case 9: return gemv_wave_dt<2, 1, FUSED>(p, x, xd, signs, y, st, sa);
     case 10: return gemv_wave_dt<2, 2, FUSED>(p, x, xd, signs, y, st, sa);
-    default: return gemv_wave_dt<2, 3, FUSED>(p, x, xd, signs, y, st, sa);
+    case 11: return gemv_wave_dt<2, 3, FUSED>(p, x, xd, signs, y, st, sa);
+    default: break;
   }
+  if constexpr (!FUSED) {
+    switch (p.k / 1024) {
+      case 12: return gemv_wave_dt<3, 0, false>(p, x, xd, signs, y, st, sa);
+      case 13: return gemv_wave_dt<3, 1, false>(p, x, xd, signs, y, st, sa);
+      case 14: return gemv_wave_dt<3, 2, false>(p, x, xd, signs, y, st, sa);
+      case 15: return gemv_wave_dt<3, 3, false>(p, x, xd, signs, y, st, sa);
+      case 16: return gemv_wave_dt<4, 0, false>(p, x, xd, signs, y, st, sa);
+      default: return gemv_wave_dt<4, 1, false>(p, x, xd, signs, y, st, sa);
+    }
+  }
+  return hipErrorInvalidValue;  // not reached: the fused step is checked for m <= 11
 }
 
 // Teams per workgroup: fewest idle lanes, then the smallest workgroup.
@@ -653,7 +666,7 @@ hipError_t launch_gemv(const Planes &p, const void *x, int xd, int64_t batch, in
   // a chunk never spans two groups (64 | 128); wide rows need wider chunks
   const bool wide32 = p.k / 32 > 1024, wide16 = p.k / 16 > 1024;
   if (batch >= 2 && gemv_quads_fits(p)) return launch_gemv_quads(p, x, xd, batch, ldx, y, ldy, st);
-  if (batch <= 1 && gemv_wave_fits(p)) return gemv_wave<false>(p, x, xd, nullptr, y, st);
+  if (batch <= 1 && gemv_wave_fits(p, false)) return gemv_wave<false>(p, x, xd, nullptr, y, st);
   if (batch <= 1 || (wide32 && batch <= 2)) {
     if (batch <= 1) return gemv_b1<FMT_PQ2, 64>(p, x, xd, ldx, y, ldy, st);
     return gemv_go<FMT_PQ2, 64, 2, 2>(p, x, xd, batch, ldx, y, ldy, st);
@@ -669,7 +682,7 @@ hipError_t launch_gemv(const Planes &p, const void *x, int xd, int64_t batch, in
 }
 
 bool rotated_gemv_fused(const Planes &p, int64_t batch) {
-  return batch == 1 && gemv_wave_fits(p);
+  return batch == 1 && gemv_wave_fits(p, true);
 }
 
 hipError_t launch_rotated_gemv(const Planes &p, const void *x, int xd, const uint16_t *signs,
