@@ -19,7 +19,9 @@ SHAPES = [("PQ2_0_G128", 3, 200), ("PTQ1_0_G128", 3, 200), ("PQ2_0_G128", 7, 102
           ("PTQ1_0_G128", 1000, 5120), ("PQ2_0_G128", 17408, 5120), ("PTQ1_0_G128", 5120, 17408),
           # odd block counts (PQ2_0 blocks move in pairs, the last one alone)
           ("PQ2_0_G128", 1, 128), ("PQ2_0_G128", 3, 384), ("PQ2_0_G128", 1001, 640),
-          ("PTQ1_0_G128", 1, 128)]
+          ("PTQ1_0_G128", 1, 128),
+          # the vocabulary head's stream, as the bench transcodes it
+          ("PQ2_0_G128", 248320, 5120)]
 
 
 @pytest.mark.parametrize("fmt,n,k", SHAPES)
