@@ -67,6 +67,16 @@ tq_status geometry(int32_t format, int64_t n, int64_t k, tq_geometry *g) {
   if (n < 1 || k < 1)
     return fail(TQ_ERR_SHAPE, "shape must be rank 2 with positive dimensions "
                 "(got n=%lld, k=%lld)", (long long)n, (long long)k);
+  // every size below must fit 64 bits: the largest, the payload, is under
+  // n * (k_pad / 128) * 28 + 512 bytes, so bound that product by 2^62
+  {
+    const uint64_t groups = ((uint64_t)k + kGroup - 1) / kGroup;
+    uint64_t rowb = 0, all = 0;
+    if (__builtin_mul_overflow(groups, (uint64_t)(f.base + f.high + 2), &rowb) ||
+        __builtin_mul_overflow(rowb, (uint64_t)n, &all) || all > (uint64_t(1) << 62))
+      return fail(TQ_ERR_SHAPE, "shape n=%lld, k=%lld is too large: its payload does not fit "
+                  "64-bit sizes", (long long)n, (long long)k);
+  }
   g->n = (uint64_t)n;
   g->k = (uint64_t)k;
   g->k_pad = align_up(g->k, kGroup);

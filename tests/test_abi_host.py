@@ -95,6 +95,14 @@ def test_host_errors():
     assert "unknown numeric format" in msg
     expect_error(5, tq.geometry, "PQ2_0_G128", 0, 128)
     expect_error(5, tq.geometry, "PQ2_0_G128", 4, -1)
+    # sizes that would wrap 64-bit arithmetic are refused, not wrapped
+    for fmt in FMTS:
+        msg = expect_error(5, tq.geometry, fmt, 1 << 62, 1 << 20)
+        assert "too large" in msg
+        expect_error(5, tq.geometry, fmt, (1 << 40) + 1, 1 << 25)
+    # the largest accepted payload is bounded by 2^62 bytes
+    g = tq.geometry("PQ2_0_G128", 1 << 30, 1 << 20)
+    assert g["payload_bytes"] < (1 << 63)
     bad = np.full((2, 128), 2, np.int8)
     expect_error(8, tq.pack_rowsplit, "PQ2_0_G128", bad, np.zeros((2, 1), np.uint16))
     # payload size mismatch: message in the pages' style
