@@ -7,15 +7,20 @@
 // block b owns bytes [b*base, (b+1)*base) of the base plane and the b-th
 // entry of the high and scale planes.
 //
-// Each thread moves whole blocks, reading every source byte once and
-// writing every destination byte once (HBM-bound: algorithmic bytes =
-// block stream + payload).  PTQ1_0 blocks are 28 bytes, so one block is
-// seven aligned dwords.  PQ2_0 blocks are 34 bytes, so a thread takes a pair
-// (68 bytes = 17 aligned dwords): the first block's 32 base bytes sit 2
-// bytes past a dword boundary and are realigned with byte permutes, the
-// second block's lie on dword boundaries.  An odd last PQ2_0 block is moved
-// by one thread on its own.  The padding between planes (less than 256
-// bytes before each plane) is written as zero by the first workgroup.
+// A workgroup moves a tile of TILE = 1024 consecutive blocks through LDS, so
+// that both sides stay contiguous across lanes: the tile's span of the block
+// stream is read (or written) as 8-byte words, lane after lane, and its
+// spans of the three planes as 16-byte chunks (base) and 4-byte words (high,
+// scale), lane after lane.  Every source byte is read once and every
+// destination byte written once (HBM-bound: algorithmic bytes = block stream
+// + payload).  In LDS the tile sits in block-stream order; a plane chunk is
+// gathered from (or scattered to) it at the block's offsets.  PQ2_0 blocks
+// are 34 bytes, so an even block's codes start 2 bytes past a dword boundary
+// and are realigned with byte shifts; PTQ1_0 blocks are 7 whole dwords.  The
+// last, partial tile moves its block-stream span 2 bytes at a time (34 * R
+// bytes need not fill whole words) and writes a lone last half-pair of the
+// 2-byte planes alone.  The padding between planes (less than 256 bytes
+// before each plane) is written as zero by the first workgroup.
 
 #include "tq_device.h"
 #include "tq_launch.h"
@@ -23,116 +28,194 @@
 namespace tq {
 namespace {
 
+constexpr int TILE = 1024;  // blocks per tile
+constexpr int TPB = 256;    // threads per workgroup
+
 struct PlaneOffsets {
   uint64_t base_bytes, high_offset, high_bytes, scale_offset, scale_bytes, payload_bytes, blocks_bytes;
 };
 
-// bytes 2..5 of the pair (lo, hi): a dword that starts 2 bytes into lo
-__device__ __forceinline__ uint32_t shift2(uint32_t lo, uint32_t hi) {
-  return __builtin_amdgcn_perm(hi, lo, 0x05040302u);
+template <int FMT>
+struct BlockShape {
+  static constexpr int BYTES = FMT == FMT_PQ2 ? 34 : 28;  // block stream bytes per block
+  static constexpr int BASE = FMT == FMT_PQ2 ? 32 : 24;   // base plane bytes per block
+  static constexpr int TBYTES = BYTES * TILE;             // a tile of the block stream
+};
+
+// LDS byte offset of the b-th block's base byte 0 inside the tile
+template <int FMT>
+__device__ __forceinline__ int base_at(int b) {
+  return FMT == FMT_PQ2 ? 34 * b + 2 : 28 * b;
 }
 
 template <int FMT, bool TO_PLANES>
-__global__ __launch_bounds__(256) void transcode_kernel(const uint8_t *__restrict__ src,
+__global__ __launch_bounds__(TPB) void transcode_kernel(const uint8_t *__restrict__ src,
                                                         uint8_t *__restrict__ dst, PlaneOffsets g) {
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  using S = BlockShape<FMT>;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[S::TBYTES / 4 + 4];
+  uint16_t *lds16 = reinterpret_cast<uint16_t *>(lds);
+  const int t = threadIdx.x;
+  const uint64_t blocks = g.blocks_bytes / S::BYTES;
+  const uint64_t tiles = (blocks + TILE - 1) / TILE;
+
   if (TO_PLANES && blockIdx.x == 0) {
     // zero the padding between the planes
     const uint64_t pad1 = g.high_offset - g.base_bytes;
     const uint64_t hend = g.high_offset + g.high_bytes;
     const uint64_t pad2 = g.scale_offset - hend;
-    for (uint64_t i = threadIdx.x; i < pad1 + pad2; i += blockDim.x)
-      dst[i < pad1 ? g.base_bytes + i : hend + (i - pad1)] = 0;
+    for (uint64_t i = t; i < pad1 + pad2; i += TPB) dst[i < pad1 ? g.base_bytes + i : hend + (i - pad1)] = 0;
   }
-  if constexpr (FMT == FMT_PTQ1) {
-    const uint64_t blocks = g.blocks_bytes / 28;
-    for (uint64_t b = tid; b < blocks; b += stride) {
-      uint32_t *bw = reinterpret_cast<uint32_t *>(TO_PLANES ? nullptr : dst + 28 * b);
-      u32x2 *pb = reinterpret_cast<u32x2 *>((TO_PLANES ? dst : const_cast<uint8_t *>(src)) + 24 * b);
-      uint16_t *ph = reinterpret_cast<uint16_t *>((TO_PLANES ? dst : const_cast<uint8_t *>(src)) +
-                                                  g.high_offset + 2 * b);
-      uint16_t *ps = reinterpret_cast<uint16_t *>((TO_PLANES ? dst : const_cast<uint8_t *>(src)) +
-                                                  g.scale_offset + 2 * b);
-      if constexpr (TO_PLANES) {
-        const uint32_t *w = reinterpret_cast<const uint32_t *>(src + 28 * b);
-        uint32_t v[7];
+
+  // the tile's stretches: block stream, base plane, and the 2-byte planes
+  // (high for PTQ1_0, scale for both)
+  const uint8_t *blk_src = TO_PLANES ? src : nullptr;
+  uint8_t *blk_dst = TO_PLANES ? nullptr : dst;
+  const uint8_t *pay_src = TO_PLANES ? nullptr : src;
+  uint8_t *pay_dst = TO_PLANES ? dst : nullptr;
+
+  for (uint64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const uint64_t b0 = tile * TILE;
+    const int R = (int)(blocks - b0 < (uint64_t)TILE ? blocks - b0 : (uint64_t)TILE);  // blocks here
+    const bool full = R == TILE;
+    const uint64_t bs_off = b0 * S::BYTES, base_off = b0 * S::BASE;
+    // words of 2 bytes per block: u covers blocks 2u, 2u+1
+    auto two_byte_planes = [&](auto fn) {
+      for (int u = t; 2 * u < R; u += TPB) fn(u, 2 * u + 1 < R);
+    };
+
+    if constexpr (TO_PLANES) {
+      // ---- block stream -> LDS
+      if (full) {
+        const u32x2 *s8 = reinterpret_cast<const u32x2 *>(blk_src + bs_off);
+        u32x2 *l8 = reinterpret_cast<u32x2 *>(lds);
 #pragma unroll
-        for (int i = 0; i < 7; ++i) v[i] = w[i];
-        pb[0] = (u32x2){v[0], v[1]};
-        pb[1] = (u32x2){v[2], v[3]};
-        pb[2] = (u32x2){v[4], v[5]};
-        *ph = (uint16_t)v[6];
-        *ps = (uint16_t)(v[6] >> 16);
+        for (int j = 0; j < S::TBYTES / 8 / TPB; ++j) l8[t + TPB * j] = s8[t + TPB * j];
       } else {
-        const u32x2 a = pb[0], c = pb[1], d = pb[2];
-        const uint32_t hs = (uint32_t)*ph | ((uint32_t)*ps << 16);
-        const uint32_t v[7] = {a[0], a[1], c[0], c[1], d[0], d[1], hs};
+        const uint16_t *s2 = reinterpret_cast<const uint16_t *>(blk_src + bs_off);
+        for (int i = t; i < R * S::BYTES / 2; i += TPB) lds16[i] = s2[i];
+      }
+      __syncthreads();
+      // ---- base plane: 16-byte chunks c (a partial last chunk as 8 bytes)
+      const int base_len = R * S::BASE;
+      u32x4 *pb = reinterpret_cast<u32x4 *>(pay_dst + base_off);
+      for (int c = t; 16 * c < base_len; c += TPB) {
+        uint32_t w[4];
+        if constexpr (FMT == FMT_PQ2) {
+          const int off = base_at<FMT>(c >> 1) + 16 * (c & 1);
+          const int a = off >> 2, sh = off & 3;  // sh is 0 or 2
+          const uint32_t d0 = lds[a], d1 = lds[a + 1], d2 = lds[a + 2], d3 = lds[a + 3], d4 = lds[a + 4];
+          w[0] = __builtin_amdgcn_alignbyte(d1, d0, sh);
+          w[1] = __builtin_amdgcn_alignbyte(d2, d1, sh);
+          w[2] = __builtin_amdgcn_alignbyte(d3, d2, sh);
+          w[3] = __builtin_amdgcn_alignbyte(d4, d3, sh);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 7; ++i) bw[i] = v[i];
+          for (int j = 0; j < 4; ++j) {
+            const int i = 16 * c + 4 * j;  // base byte of the tile, a multiple of 4
+            w[j] = lds[7 * (i / 24) + (i % 24) / 4];
+          }
+        }
+        if (16 * c + 16 <= base_len)
+          pb[c] = (u32x4){w[0], w[1], w[2], w[3]};
+        else
+          *reinterpret_cast<u32x2 *>(pb + c) = (u32x2){w[0], w[1]};
+      }
+      // ---- 2-byte planes
+      uint32_t *ps = reinterpret_cast<uint32_t *>(pay_dst + g.scale_offset + 2 * b0);
+      uint32_t *ph = reinterpret_cast<uint32_t *>(pay_dst + g.high_offset + 2 * b0);
+      two_byte_planes([&](int u, bool pair) {
+        uint32_t sc, hi = 0;
+        if constexpr (FMT == FMT_PQ2) {
+          // scales at bytes 34b: the low half of dword 17u, the high half of 17u + 8
+          sc = (lds[17 * u] & 0xFFFFu) | (lds[17 * u + 8] & 0xFFFF0000u);
+        } else {
+          const uint32_t e0 = lds[14 * u + 6], e1 = lds[14 * u + 13];  // [high | scale] of 2u, 2u+1
+          hi = (e0 & 0xFFFFu) | (e1 << 16);
+          sc = (e0 >> 16) | (e1 & 0xFFFF0000u);
+        }
+        if (pair) {
+          ps[u] = sc;
+          if constexpr (FMT == FMT_PTQ1) ph[u] = hi;
+        } else {
+          reinterpret_cast<uint16_t *>(ps)[2 * u] = (uint16_t)sc;
+          if constexpr (FMT == FMT_PTQ1) reinterpret_cast<uint16_t *>(ph)[2 * u] = (uint16_t)hi;
+        }
+      });
+    } else {
+      // ---- base plane -> LDS
+      const int base_len = R * S::BASE;
+      const u32x4 *pb = reinterpret_cast<const u32x4 *>(pay_src + base_off);
+      for (int c = t; 16 * c < base_len; c += TPB) {
+        u32x4 v;
+        if (16 * c + 16 <= base_len) {
+          v = pb[c];
+        } else {
+          const u32x2 h = *reinterpret_cast<const u32x2 *>(pb + c);
+          v = (u32x4){h[0], h[1], 0u, 0u};
+        }
+        const int nw = 16 * c + 16 <= base_len ? 4 : 2;
+        if constexpr (FMT == FMT_PQ2) {
+          const int off = base_at<FMT>(c >> 1) + 16 * (c & 1);
+          if ((off & 3) == 0) {
+            for (int j = 0; j < nw; ++j) lds[(off >> 2) + j] = v[j];
+          } else {
+            // 2 bytes past a dword boundary: a half word, whole realigned
+            // words, and a closing half word
+            lds16[off >> 1] = (uint16_t)v[0];
+            for (int j = 0; j + 1 < nw; ++j) lds[(off + 2) / 4 + j] = (v[j] >> 16) | (v[j + 1] << 16);
+            lds16[(off >> 1) + 2 * nw - 1] = (uint16_t)(v[nw - 1] >> 16);
+          }
+        } else {
+          for (int j = 0; j < nw; ++j) {
+            const int i = 16 * c + 4 * j;
+            lds[7 * (i / 24) + (i % 24) / 4] = v[j];
+          }
+        }
+      }
+      const uint32_t *ps = reinterpret_cast<const uint32_t *>(pay_src + g.scale_offset + 2 * b0);
+      const uint32_t *ph = reinterpret_cast<const uint32_t *>(pay_src + g.high_offset + 2 * b0);
+      two_byte_planes([&](int u, bool pair) {
+        const uint16_t *ps2 = reinterpret_cast<const uint16_t *>(ps);
+        const uint16_t *ph2 = reinterpret_cast<const uint16_t *>(ph);
+        const uint32_t sc = pair ? ps[u] : ps2[2 * u];
+        if constexpr (FMT == FMT_PQ2) {
+          lds16[17 * (2 * u)] = (uint16_t)sc;  // byte 34b, b = 2u
+          if (pair) lds16[17 * (2 * u + 1)] = (uint16_t)(sc >> 16);
+        } else {
+          const uint32_t hi = pair ? ph[u] : ph2[2 * u];
+          lds[14 * u + 6] = (hi & 0xFFFFu) | (sc << 16);
+          if (pair) lds[14 * u + 13] = (hi >> 16) | (sc & 0xFFFF0000u);
+        }
+      });
+      __syncthreads();
+      // ---- LDS -> block stream
+      if (full) {
+        u32x2 *d8 = reinterpret_cast<u32x2 *>(blk_dst + bs_off);
+        const u32x2 *l8 = reinterpret_cast<const u32x2 *>(lds);
+#pragma unroll
+        for (int j = 0; j < S::TBYTES / 8 / TPB; ++j) d8[t + TPB * j] = l8[t + TPB * j];
+      } else {
+        uint16_t *d2 = reinterpret_cast<uint16_t *>(blk_dst + bs_off);
+        for (int i = t; i < R * S::BYTES / 2; i += TPB) d2[i] = lds16[i];
       }
     }
-  } else {
-    const uint64_t blocks = g.blocks_bytes / 34, pairs = blocks / 2;
-    for (uint64_t p = tid; p < pairs; p += stride) {
-      uint32_t *pbase = reinterpret_cast<uint32_t *>((TO_PLANES ? dst : const_cast<uint8_t *>(src)) + 64 * p);
-      uint32_t *pscale = reinterpret_cast<uint32_t *>((TO_PLANES ? dst : const_cast<uint8_t *>(src)) +
-                                                      g.scale_offset + 4 * p);
-      if constexpr (TO_PLANES) {
-        // w[0] = [s0 | c0 c1], w[1..7], w[8] = [c30 c31 | s1], w[9..16] = block 2p+1's codes
-        const uint32_t *s = reinterpret_cast<const uint32_t *>(src + 68 * p);
-        uint32_t w[17];
-#pragma unroll
-        for (int i = 0; i < 17; ++i) w[i] = s[i];
-        u32x4 *ob = reinterpret_cast<u32x4 *>(pbase);
-        ob[0] = (u32x4){shift2(w[0], w[1]), shift2(w[1], w[2]), shift2(w[2], w[3]), shift2(w[3], w[4])};
-        ob[1] = (u32x4){shift2(w[4], w[5]), shift2(w[5], w[6]), shift2(w[6], w[7]), shift2(w[7], w[8])};
-        ob[2] = (u32x4){w[9], w[10], w[11], w[12]};
-        ob[3] = (u32x4){w[13], w[14], w[15], w[16]};
-        *pscale = (w[0] & 0xFFFFu) | (w[8] & 0xFFFF0000u);
-      } else {
-        const u32x4 *ib = reinterpret_cast<const u32x4 *>(pbase);
-        const u32x4 q0 = ib[0], q1 = ib[1], q2 = ib[2], q3 = ib[3];
-        const uint32_t c[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-        const uint32_t sc = *pscale;
-        uint32_t *o = reinterpret_cast<uint32_t *>(dst + 68 * p);
-        o[0] = (sc & 0xFFFFu) | (c[0] << 16);
-#pragma unroll
-        for (int i = 1; i < 8; ++i) o[i] = shift2(c[i - 1], c[i]);
-        o[8] = (c[7] >> 16) | (sc & 0xFFFF0000u);
-        o[9] = q2[0]; o[10] = q2[1]; o[11] = q2[2]; o[12] = q2[3];
-        o[13] = q3[0]; o[14] = q3[1]; o[15] = q3[2]; o[16] = q3[3];
-      }
-    }
-    // an odd last block, 34 bytes from a dword boundary (its index is even)
-    if ((blocks & 1) && tid == pairs % stride) {
-      const uint64_t b = blocks - 1;
-      const uint16_t *s16 = reinterpret_cast<const uint16_t *>(src);
-      uint16_t *d16 = reinterpret_cast<uint16_t *>(dst);
-      if constexpr (TO_PLANES) {
-        for (int i = 0; i < 16; ++i) d16[(32 * b) / 2 + i] = s16[(34 * b) / 2 + 1 + i];
-        d16[(g.scale_offset + 2 * b) / 2] = s16[(34 * b) / 2];
-      } else {
-        d16[(34 * b) / 2] = s16[(g.scale_offset + 2 * b) / 2];
-        for (int i = 0; i < 16; ++i) d16[(34 * b) / 2 + 1 + i] = s16[(32 * b) / 2 + i];
-      }
-    }
+    __syncthreads();  // the tile's LDS is read before the next tile overwrites it
   }
 }
 
 template <bool TO_PLANES>
 hipError_t transcode_go(int fmt, const uint8_t *src, uint8_t *dst, const PlaneOffsets &g,
                         hipStream_t st) {
-  const uint64_t items = fmt == FMT_PQ2 ? (g.blocks_bytes / 34 + 1) / 2 : g.blocks_bytes / 28;
-  uint64_t wgs = (items + 255) / 256;
-  const uint64_t cap = (uint64_t)device_cus() * 16;  // a grid-stride loop beyond that
+  const uint64_t blocks = g.blocks_bytes / (fmt == FMT_PQ2 ? 34 : 28);
+  uint64_t wgs = (blocks + TILE - 1) / TILE;
+  const uint64_t cap = (uint64_t)device_cus() * 64;  // a grid-stride loop over tiles beyond that
   if (wgs > cap) wgs = cap;
   if (wgs == 0) wgs = 1;  // (the padding is still written)
   if (fmt == FMT_PQ2)
-    hipLaunchKernelGGL((transcode_kernel<FMT_PQ2, TO_PLANES>), dim3((unsigned)wgs), dim3(256), 0, st,
+    hipLaunchKernelGGL((transcode_kernel<FMT_PQ2, TO_PLANES>), dim3((unsigned)wgs), dim3(TPB), 0, st,
                        src, dst, g);
   else
-    hipLaunchKernelGGL((transcode_kernel<FMT_PTQ1, TO_PLANES>), dim3((unsigned)wgs), dim3(256), 0,
+    hipLaunchKernelGGL((transcode_kernel<FMT_PTQ1, TO_PLANES>), dim3((unsigned)wgs), dim3(TPB), 0,
                        st, src, dst, g);
   return hipGetLastError();
 }
