@@ -10,7 +10,10 @@
 // weights, one scale) becomes blocks 2g and 2g+1, both with that scale.
 //
 // Expansion (HBM-bound byte reshuffle): one thread per group reads the
-// group's code bytes and scale and writes its two blocks (36 bytes).  PQ2_0
+// group's code bytes and scale and builds its two blocks (36 bytes) in LDS;
+// a workgroup gathers a tile of GT consecutive groups there and writes the
+// tile's 36 * GT output bytes as 16-byte chunks, lane after lane (a 36-byte
+// stride per lane would scatter every store instruction over many lines).  PQ2_0
 // code bytes are already the 2-bit codes, in the same order.  A PTQ1_0 digit
 // is trit + 1, which is the 2-bit code: a 256-entry LDS table gives the five
 // digits of a base byte as five 2-bit fields (the four of a high byte are its
@@ -24,6 +27,8 @@
 namespace tq {
 
 namespace {
+
+constexpr int GT = 1024;  // groups per expansion tile
 
 // Two blocks of one group from its 32 code bytes c[0..7] (little-endian
 // dwords) and its scale bits s: 9 dwords, [s | c0 c1], [c2..c5], ..,
@@ -58,39 +63,59 @@ __global__ __launch_bounds__(256) void expand_g64_kernel(const uint8_t *__restri
     lut[t] = (uint16_t)f;
     __syncthreads();
   }
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += stride) {
-    uint32_t c[8];
-    if constexpr (FMT == FMT_PQ2) {
-      const u32x4 *b = reinterpret_cast<const u32x4 *>(base + 32 * g);
-      const u32x4 lo = b[0], hi = b[1];
-      c[0] = lo[0]; c[1] = lo[1]; c[2] = lo[2]; c[3] = lo[3];
-      c[4] = hi[0]; c[5] = hi[1]; c[6] = hi[2]; c[7] = hi[3];
-    } else {
-      const u32x2 *b = reinterpret_cast<const u32x2 *>(base + 24 * g);
-      const u32x2 b0 = b[0], b1 = b[1], b2 = b[2];
-      const uint32_t bw[6] = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1]};
-      const uint32_t hw = reinterpret_cast<const uint16_t *>(high)[g];
-      uint64_t acc[4] = {0, 0, 0, 0};
+  __shared__ __attribute__((aligned(16))) uint32_t tile_out[9 * GT];
+  const int t = threadIdx.x;
+  const int64_t tiles = (groups + GT - 1) / GT;
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int64_t g0 = tile * GT;
+    const int R = (int)(groups - g0 < GT ? groups - g0 : GT);  // groups in this tile
 #pragma unroll
-      for (int bi = 0; bi < 24; ++bi) {
-        const uint64_t f = lut[(bw[bi >> 2] >> (8 * (bi & 3))) & 0xFFu];
-        const int pos = 10 * bi;  // trits 5bi.. -> code bits 10bi..
-        acc[pos >> 6] |= f << (pos & 63);
-        if ((pos & 63) > 54) acc[(pos >> 6) + 1] |= f >> (64 - (pos & 63));
-      }
+    for (int j = 0; j < GT / 256; ++j) {
+      const int gl = t + 256 * j;
+      if (gl >= R) continue;
+      const int64_t g = g0 + gl;
+      uint32_t c[8];
+      if constexpr (FMT == FMT_PQ2) {
+        const u32x4 *b = reinterpret_cast<const u32x4 *>(base + 32 * g);
+        const u32x4 lo = b[0], hi = b[1];
+        c[0] = lo[0]; c[1] = lo[1]; c[2] = lo[2]; c[3] = lo[3];
+        c[4] = hi[0]; c[5] = hi[1]; c[6] = hi[2]; c[7] = hi[3];
+      } else {
+        const u32x2 *b = reinterpret_cast<const u32x2 *>(base + 24 * g);
+        const u32x2 b0 = b[0], b1 = b[1], b2 = b[2];
+        const uint32_t bw[6] = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1]};
+        const uint32_t hw = reinterpret_cast<const uint16_t *>(high)[g];
+        uint64_t acc[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {  // trits 120+4h.. -> code bits 240+8h..
-        const uint64_t f = lut[(hw >> (8 * h)) & 0xFFu] & 0xFFu;
-        acc[3] |= f << (48 + 8 * h);
-      }
+        for (int bi = 0; bi < 24; ++bi) {
+          const uint64_t f = lut[(bw[bi >> 2] >> (8 * (bi & 3))) & 0xFFu];
+          const int pos = 10 * bi;  // trits 5bi.. -> code bits 10bi..
+          acc[pos >> 6] |= f << (pos & 63);
+          if ((pos & 63) > 54) acc[(pos >> 6) + 1] |= f >> (64 - (pos & 63));
+        }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c[2 * i] = (uint32_t)acc[i];
-        c[2 * i + 1] = (uint32_t)(acc[i] >> 32);
+        for (int h = 0; h < 2; ++h) {  // trits 120+4h.. -> code bits 240+8h..
+          const uint64_t f = lut[(hw >> (8 * h)) & 0xFFu] & 0xFFu;
+          acc[3] |= f << (48 + 8 * h);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          c[2 * i] = (uint32_t)acc[i];
+          c[2 * i + 1] = (uint32_t)(acc[i] >> 32);
+        }
       }
+      store_two_blocks(tile_out + 9 * gl, c, scale[g]);
     }
-    store_two_blocks(reinterpret_cast<uint32_t *>(out + 36 * g), c, scale[g]);
+    __syncthreads();
+    uint8_t *o = out + 36 * g0;
+    if (R == GT) {
+#pragma unroll
+      for (int j = 0; j < 9 * GT / 4 / 256; ++j)
+        reinterpret_cast<u32x4 *>(o)[t + 256 * j] = reinterpret_cast<const u32x4 *>(tile_out)[t + 256 * j];
+    } else {
+      for (int i = t; i < 9 * R; i += 256) reinterpret_cast<uint32_t *>(o)[i] = tile_out[i];
+    }
+    __syncthreads();  // the tile is written out before the next one is built
   }
 }
 
@@ -123,8 +148,8 @@ hipError_t launch_expand_g64(int fmt, const uint8_t *base, const uint8_t *high,
                              const uint16_t *scale, uint8_t *out, int64_t groups,
                              hipStream_t st) {
   if (groups <= 0) return hipSuccess;
-  const int64_t want = (groups + 255) / 256;
-  const int64_t cap = (int64_t)device_cus() * 32;
+  const int64_t want = (groups + GT - 1) / GT;
+  const int64_t cap = (int64_t)device_cus() * 64;
   const unsigned grid = (unsigned)(want < cap ? want : cap);
   if (fmt == FMT_PQ2)
     hipLaunchKernelGGL(expand_g64_kernel<FMT_PQ2>, dim3(grid), dim3(256), 0, st, base, high, scale,
