@@ -86,6 +86,27 @@ def test_hadamard_in_place_strided_and_stream():
     assert tq.hadamard_signed(empty, signs_dev(torch, sbits)).shape == (0, k)
 
 
+@pytest.mark.parametrize("xdt,ydt,inverse,rows,k,in_place",
+                         [("bf16", "f16", 0, 3001, 3072, False), ("f32", "f32", 1, 2500, 2048, True),
+                          ("f16", "f16", 0, 4099, 1024, True)])
+def test_hadamard_many_rows(xdt, ydt, inverse, rows, k, in_place):
+    """More blocks than the launch has waves: each wave transforms several
+    blocks in turn (its next block requested before the current one is
+    stored), with a ragged last round; in place too."""
+    rng = np.random.default_rng(rows + k)
+    sbits = synth.sign_bits(rng, k)
+    x = rand_x(rng, rows, k, xdt, scale=2.0)
+    say("hadamard many rows %s->%s inverse=%d rows=%d k=%d in_place=%s" % (xdt, ydt, inverse, rows, k, in_place))
+    xd = x_dev(torch, x, xdt)
+    kw = dict(out=xd) if in_place else dict(out_dtype=getattr(torch, TORCH_DT[ydt]))
+    y = tq.hadamard_signed(xd, signs_dev(torch, sbits), inverse=bool(inverse), **kw)
+    torch.cuda.synchronize()
+    xf = x_f64(x, xdt)
+    expect = (T.inverse if inverse else T.forward)(xf, T.bf16_bits_to_f64(sbits))
+    bound = 1e-3 * T.block_l1_over_32(xf) + 1e-5 + ROUND[ydt] * np.abs(expect)
+    assert_within(to_f64(torch, y), expect, bound, "hadamard many rows")
+
+
 # ------------------------------------------------------------ decode hook --
 @pytest.mark.parametrize("fmt", ["PQ2_0_G128", "PTQ1_0_G128"])
 def test_decode_bit_exact(fmt):
