@@ -47,25 +47,6 @@ def expanded_bytes(n, k):
     return n * blocks_per_row(k) * BLOCK_BYTES
 
 
-def expanded_bytes(n, k):
-    """Size of the expanded stream of an n x k matrix."""
-    return n * blocks_per_row(k) * BLOCK_BYTES
-
-
-def encode_block(trits, scale_bits):
-    """64 trits and the binary16 bits of d -> one 18-byte block."""
-    assert len(trits) == BLOCK_WEIGHTS
-    out = bytearray(BLOCK_BYTES)
-    out[0] = scale_bits & 0xFF
-    out[1] = (scale_bits >> 8) & 0xFF
-    for j, t in enumerate(trits):
-        t = int(t)
-        if t not in (-1, 0, 1):
-            raise ValueError("trit out of range: %d" % t)
-        out[2 + j // 4] |= (t + 1) << (2 * (j % 4))
-    return bytes(out)
-
-
 def expand(fmt, n, k, payload):
     """Row-split planes of either ternary format -> the G64 block stream.
 

@@ -104,3 +104,37 @@ def test_bit_conversions():
 def test_rejects_partial_block(k):
     with pytest.raises(ValueError):
         T.forward(np.zeros((1, k)), np.ones(k))
+
+
+def test_block_l1_over_32_hand_values():
+    # The scale of the transform tolerance: per element, the L1 norm of the
+    # 1024-element block holding it, over 32 (sum_j |H_ij d_j x_j| / 32 with
+    # |H_ij d_j| = 1).  Hand-computed cases: a block of ones gives 1024/32;
+    # a block whose only nonzeros are 3 and -4 gives 7/32 (an L2 norm would
+    # give 5/32); blocks and rows stay separate (a per-row sum would mix them).
+    x = np.zeros((2, 2048))
+    x[0, :1024] = 1.0
+    x[0, 1024 + 5] = 3.0
+    x[0, 1024 + 900] = -4.0
+    x[1, 2047] = -0.5
+    got = T.block_l1_over_32(x)
+    assert got.shape == x.shape
+    assert np.all(got[0, :1024] == 32.0)
+    assert np.all(got[0, 1024:] == 7.0 / 32.0)
+    assert np.all(got[1, :1024] == 0.0)
+    assert np.all(got[1, 1024:] == 0.5 / 32.0)
+
+
+def test_block_l1_over_32_bounds_the_transform():
+    # Every output of the transform is at most the block's L1 norm over 32
+    # (|H_ij| = 1), with equality where the signs line up: x = d restricted to
+    # a block maps its first element to ||x||_1 / 32 exactly.
+    rng = np.random.default_rng(4)
+    d = rand_signs(rng, 2048)
+    x = rng.standard_normal((3, 2048))
+    assert np.all(np.abs(T.forward(x, d)) <= T.block_l1_over_32(x) * (1 + 1e-12))
+    v = np.abs(rng.standard_normal((1, 2048))) * d
+    f = T.forward(v, d)
+    l1 = T.block_l1_over_32(v)
+    assert np.isclose(f[0, 0], l1[0, 0], rtol=1e-13)
+    assert np.isclose(f[0, 1024], l1[0, 1024], rtol=1e-13)
