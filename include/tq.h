@@ -369,6 +369,19 @@ tq_status tq_decode_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
                              int8_t *values, uint16_t *scale_bits,
                              void *stream);
 
+/* Measurement reference (not part of the projection): read `bytes` bytes of
+ * device memory at `src` once, in 16-byte non-temporal loads from a one-shot
+ * grid of 256-thread workgroups, each thread reading four 16-byte words of
+ * its workgroup's contiguous span.  This is the access the decode GEMVs'
+ * weight stream makes, without the decode, so its duration at a given size
+ * is the read floor those kernels are compared with (decode is
+ * bandwidth-bound: [gguf-explainer] §4.8).  The loaded words are folded
+ * into one value that is stored to *sink (device uint32) only if it equals
+ * a fixed constant; the caller owns sink and ignores its contents.
+ * Requirements: bytes a positive multiple of 16 below 2^40 (TQ_ERR_SHAPE);
+ * src 16-byte and sink 4-byte aligned (TQ_ERR_ALIGN); non-NULL (TQ_ERR_ARG). */
+tq_status tq_stream_read(const void *src, uint64_t bytes, uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

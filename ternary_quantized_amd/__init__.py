@@ -41,7 +41,7 @@ EXPORTS = (
     "tq_rotated_gemv_rowsplit", "tq_blocks_to_planes", "tq_planes_to_blocks",
     "tq_container_parse", "tq_container_object_at", "tq_g64_bytes", "tq_expand_g64",
     "tq_gemv_g64", "tq_head_argmax", "tq_hadamard_signed_grouped",
-    "tq_rotated_gemv_rowsplit_grouped",
+    "tq_rotated_gemv_rowsplit_grouped", "tq_stream_read",
 )
 
 
@@ -102,6 +102,7 @@ def lib():
             "tq_rotated_gemv_rowsplit_grouped": [_vp, _u64, _i32, _i64, _i64, _vp, _i32, _i64, _i64,
                                                  _i32, _i32, _i32, _vp, _vp, _i64, _vp],
             "tq_gemv_g64": [_vp, _u64, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _i64, _vp],
+            "tq_stream_read": [_vp, _u64, _vp, _vp],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -433,3 +434,15 @@ def rotated_gemv_rowsplit_grouped(payload, fmt, n, k, x, signs, tiles=GDN_TILES,
         _dtype_code(x), batch, x.stride(0), tiles, groups, head_dim, _signs_ptr(signs),
         out.data_ptr(), out.stride(0), _stream(x.device)))
     return out
+
+
+def stream_read(src, sink=None):
+    """Plain streaming read of a device tensor (the bandwidth reference the
+    GEMVs are measured beside); returns the sink word tensor."""
+    torch = _torch()
+    _dev(src, "src")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=src.device)
+    _check(lib().tq_stream_read(src.data_ptr(), src.numel() * src.element_size(), sink.data_ptr(),
+                                _stream(src.device)))
+    return sink

@@ -39,6 +39,23 @@ __device__ __forceinline__ uint16_t f32_to_f16(float f) {
   return b;
 }
 
+// A pair of 2-bit codes -> the pair of binary16 trits code - 1, exactly:
+// (p & mask_i) | 0x6400_6400 holds 1024 + 4^i * code in each half (i is the
+// code's 2-bit slot, 0..4), and fma(v, 4^-i, -(1024 * 4^-i + 1)) = code - 1.
+// Every value involved is a normal binary16.
+template <int I>
+__device__ __forceinline__ uint32_t trit_pair(uint32_t p, uint32_t magic_v) {
+  constexpr uint32_t mask = 0x00030003u << (2 * I);
+  constexpr float inv = I == 0 ? 1.0f : I == 1 ? 0.25f : I == 2 ? 0.0625f : I == 3 ? 0.015625f
+                                                                                   : 0.00390625f;
+  constexpr float neg = I == 0 ? -1025.0f : I == 1 ? -257.0f : I == 2 ? -65.0f : I == 3 ? -17.0f
+                                                                                        : -5.0f;
+  const half2_t t = __builtin_bit_cast(half2_t, (p & mask) | magic_v);
+  const half2_t m = {(_Float16)inv, (_Float16)inv};
+  const half2_t c = {(_Float16)neg, (_Float16)neg};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(t, m, c));
+}
+
 template <int DT>
 __device__ __forceinline__ float load_elem(const void *p, int64_t i) {
   if constexpr (DT == DT_F32) return static_cast<const float *>(p)[i];

@@ -1,22 +1,22 @@
 // Decode GEMV over row-split ternary planes:
 //   y[b][n] = sum_g s[n][g] * sum_{j in g} t[n][j] * x'[b][j]
-// [gguf-explainer] §4.3 (code semantics) and §4.4 (the dot product with an
-// offset code: d * sum (q-1) x = d * (sum q x - sum x), where sum x does not
-// depend on the weights and is computed once); [ninfer-skill] §3 (planes).
+// [gguf-explainer] §4.3 (code semantics: value = (code - 1) * d with one
+// scale per group); [ninfer-skill] §3 (planes).  This file holds the
+// persistent team kernel that serves the shapes the batch-1 wave kernel and
+// the row-quad kernel do not (rows longer than they hold), and the dispatch
+// of tq_gemv_rowsplit among the three.
 //
-// Design (gfx950, wave64):
+// Design of the team kernel (gfx950, wave64):
 //  * Every thread owns one fixed K-chunk of the row ("lane chunk") and keeps
 //    the matching activations in registers as binary16 pairs, so weights are
 //    the only data streamed from HBM; a team of ceil(C/16)*16 threads covers
 //    the C chunks of one row and a workgroup holds R teams.
-//  * Codes are unpacked with the fp4 (E2M1) converter: masking the 2-bit
-//    codes into the low half of each nibble turns a nibble into the fp4
-//    number code/2, so v_cvt_scalef32_pk_f16_fp4 with scale 2 yields the
-//    codes 0..3 as exact binary16 pairs, consumed by v_dot2_f32_f16 with fp32
-//    accumulation.  The offset -1 is applied once per chunk as
-//    s * (sum code*x - sum x).
-//  * PTQ1_0 bytes (five radix-3 digits) go through 256-entry LDS tables whose
-//    entries hold the digits as fp4 nibbles laid out for the same converter.
+//  * Codes become exact binary16 trits: a code ORed into the mantissa of
+//    1024 and one packed fma give code - 1 (trit_pair), consumed by
+//    v_dot2_f32_f16 with fp32 accumulation.  Zero weights contribute exact
+//    zeros, so the rounding error follows sum |w x'| alone.
+//  * PTQ1_0 bytes (five radix-3 digits) go through a 256-entry LDS table
+//    whose entries hold the digits as 2-bit codes, decoded the same way.
 //  * Partial sums are reduced across 16-lane segments with lane shuffles and
 //    across segments through LDS in a fixed order (no atomics: bitwise
 //    reproducible).
@@ -27,39 +27,9 @@
 
 namespace tq {
 
-__device__ __forceinline__ half2_t cvt_codes(uint32_t v, int sel) {
-  switch (sel) {
-    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 2.0f, 0);
-    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 2.0f, 1);
-    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 2.0f, 2);
-    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 2.0f, 3);
-  }
-}
-
-
 __device__ __forceinline__ float dot2(half2_t a, half2_t b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }
-
-// The first products of the five code classes, a[c] = t[c].lo*x[c].lo +
-// t[c].hi*x[c].hi, each from a zero accumulator.  They are taken in the
-// three-operand form: the compiler only emits the two-operand form, whose
-// accumulator is tied to the destination and would need five registers
-// cleared first.  A dot product's result may be read by a different vector
-// instruction only three wait states later, which the compiler cannot see
-// through the asm, so the block ends with those wait states itself.
-__device__ __forceinline__ void dot2_first5(const uint32_t (&t)[8], const half2_t *x, float (&a)[5]) {
-  asm("v_dot2_f32_f16 %0, %5, %10, 0\n\t"
-      "v_dot2_f32_f16 %1, %6, %11, 0\n\t"
-      "v_dot2_f32_f16 %2, %7, %12, 0\n\t"
-      "v_dot2_f32_f16 %3, %8, %13, 0\n\t"
-      "v_dot2_f32_f16 %4, %9, %14, 0\n\t"
-      "s_nop 2"
-      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4])
-      : "v"(t[0]), "v"(t[1]), "v"(t[2]), "v"(t[3]), "v"(t[4]),
-        "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]));
-}
-
 
 __device__ __forceinline__ half2_t pack_h2(float a, float b) {
   half2_t r;
@@ -119,9 +89,9 @@ __device__ __forceinline__ float x_elem(uint32_t w, int half) {
 }
 
 // Activation pairs of one lane chunk in the order the decoder produces
-// weight pairs, and their fp32 sum (of the binary16-rounded values).
+// weight pairs (binary16-rounded).
 template <int FMT, int CW, int XD>
-__device__ __forceinline__ float convert_x_chunk(const XRaw<FMT, CW, XD> &r, int64_t c,
+__device__ __forceinline__ void convert_x_chunk(const XRaw<FMT, CW, XD> &r, int64_t c,
                                                  half2_t xp[CW / 2]) {
   float v[CW];
 #pragma unroll
@@ -146,10 +116,6 @@ __device__ __forceinline__ float convert_x_chunk(const XRaw<FMT, CW, XD> &r, int
       for (int i = 0; i < 5; ++i) xp[5 * pp + i] = pack_h2(v[10 * pp + i], v[10 * pp + 5 + i]);
     xp[15] = pack_h2(v[30], v[31]);
   }
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < CW; ++i) s += v[i];
-  return s;
 }
 
 // Raw plane bytes of one lane chunk of one row.
@@ -284,40 +250,34 @@ __device__ __forceinline__ void load_next(Cursor<FMT, CW> &k, int64_t n, Raw<FMT
   k.row += k.srow;
 }
 
-// sum_j code_j * x_j over one lane chunk (codes 0..2 for ternary data).
+// sum_j t_j * x_j over one lane chunk, with the trits t = code - 1 made
+// exact binary16 values first (trit_pair), so that zero weights add nothing.
 template <int FMT, int CW, int B>
 __device__ __forceinline__ void chunk_dot(const Raw<FMT, CW> &r, int64_t c,
                                           const half2_t (&xp)[B][CW / 2],
                                           const uint32_t *lut, float part[B]) {
+  const uint32_t magic = 0x64006400u;  // 1024.0 in each half
+  float a[B][4];
 #pragma unroll
-  for (int b = 0; b < B; ++b) part[b] = 0.0f;
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[b][e] = 0.0f;
   if constexpr (FMT == FMT_PQ2) {
-    // A code masked in place into a binary16 with zero exponent is the exact
-    // subnormal code * 4^e * 2^-24 (e = its 2-bit slot, slots 0..4 of each
-    // half); slots 5..7 are shifted down by 10 first.  Products are summed
-    // per slot class in fp32 and rescaled by powers of two at the end.
-    float a[B][5];
-#pragma unroll
-    for (int b = 0; b < B; ++b)
-#pragma unroll
-      for (int e = 0; e < 5; ++e) a[b][e] = 0.0f;
+    // codes 0..4 of each half in place (slots 0..4), codes 5..7 shifted
+    // down by 10 (slots 0..2): pair e holds the codes (e, e+8) of the dword
 #pragma unroll
     for (int d = 0; d < CW / 16; ++d) {
       const uint32_t w = r.w[d], w10 = w >> 10;
-      const uint32_t t[8] = {w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u,
-                             w & 0x00C000C0u, w & 0x03000300u, w10 & 0x00030003u,
-                             w10 & 0x000C000Cu, w10 & 0x00300030u};
+      const uint32_t t[8] = {trit_pair<0>(w, magic), trit_pair<1>(w, magic), trit_pair<2>(w, magic),
+                             trit_pair<3>(w, magic), trit_pair<4>(w, magic), trit_pair<0>(w10, magic),
+                             trit_pair<1>(w10, magic), trit_pair<2>(w10, magic)};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
 #pragma unroll
         for (int b = 0; b < B; ++b)
-          a[b][e < 5 ? e : e - 5] = dot2(bits_h2(t[e]), xp[b][8 * d + e], a[b][e < 5 ? e : e - 5]);
+          a[b][e & 3] = dot2(bits_h2(t[e]), xp[b][8 * d + e], a[b][e & 3]);
       }
     }
-#pragma unroll
-    for (int b = 0; b < B; ++b)
-      part[b] = a[b][0] * 16777216.0f + a[b][1] * 4194304.0f + a[b][2] * 1048576.0f +
-                a[b][3] * 262144.0f + a[b][4] * 65536.0f;
   } else {
     const int q = (int)(c & 3);
     // the lane's 6 base bytes start 0 or 2 bytes into the loaded window
@@ -325,33 +285,29 @@ __device__ __forceinline__ void chunk_dot(const Raw<FMT, CW> &r, int64_t c,
     const uint64_t bytes = (q & 1) ? (win >> 16) : win;
     // lut[v]: the five radix-3 digits of byte v as 2-bit codes, digit i at
     // bits 2i.  Two bytes side by side (second one shifted up 16) give, for
-    // each digit i, a binary16 pair whose zero-exponent fields are the codes
-    // times 4^i * 2^-24: the same subnormal-class products as PQ2_0, one
-    // mask and one dot2 per two trits.
-    float a[B][5];
+    // each digit i, a pair of codes in slot i: one trit pair per two trits.
 #pragma unroll
     for (int pp = 0; pp < 3; ++pp) {
       const uint32_t dw = lut[(bytes >> (16 * pp)) & 0xFF] |
                           (lut[(bytes >> (16 * pp + 8)) & 0xFF] << 16);
+      const uint32_t t[5] = {trit_pair<0>(dw, magic), trit_pair<1>(dw, magic), trit_pair<2>(dw, magic),
+                             trit_pair<3>(dw, magic), trit_pair<4>(dw, magic)};
 #pragma unroll
       for (int i = 0; i < 5; ++i) {
-        const half2_t t = bits_h2(dw & (0x00030003u << (2 * i)));
 #pragma unroll
         for (int b = 0; b < B; ++b)
-          a[b][i] = __builtin_amdgcn_fdot2(t, xp[b][5 * pp + i], pp == 0 ? 0.0f : a[b][i], false);
+          a[b][(5 * pp + i) & 3] = dot2(bits_h2(t[i]), xp[b][5 * pp + i], a[b][(5 * pp + i) & 3]);
       }
     }
     // the chunk's two high trits: digits 2(q&1) and 2(q&1)+1 of its high
-    // byte, placed as a class-0 pair
+    // byte, placed as a slot-0 pair
     const uint32_t wh = lut[r.h & 0xFF] >> (4 * (q & 1));
-    const half2_t th = bits_h2((wh & 3u) | ((wh & 0xCu) << 14));
+    const uint32_t th = trit_pair<0>((wh & 3u) | ((wh & 0xCu) << 14), magic);
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      a[b][0] = dot2(th, xp[b][15], a[b][0]);
-      part[b] = a[b][0] * 16777216.0f + a[b][1] * 4194304.0f + a[b][2] * 1048576.0f +
-                a[b][3] * 262144.0f + a[b][4] * 65536.0f;
-    }
+    for (int b = 0; b < B; ++b) a[b][3] = dot2(bits_h2(th), xp[b][15], a[b][3]);
   }
+#pragma unroll
+  for (int b = 0; b < B; ++b) part[b] = (a[b][0] + a[b][1]) + (a[b][2] + a[b][3]);
 }
 
 // Sum over aligned segments of SEG (8 or 16) lanes inside each DPP row; the
@@ -401,9 +357,9 @@ __global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restri
                                                   int chunks, int cseg, int teams) {
   __shared__ uint32_t lut[FMT == FMT_PTQ1 ? 256 : 1];
   __shared__ float red[D * B * (1024 / SEG)];  // [slot][b][segment]
-  // activation pairs of every chunk in decode order, plus chunk sums:
-  // staged once per workgroup (teams share chunks)
-  extern __shared__ uint32_t xlds[];  // [chunk][CW/2 pairs], then [chunk] sums (one batch row)
+  // activation pairs of every chunk in decode order: staged once per
+  // workgroup (teams share chunks)
+  extern __shared__ uint32_t xlds[];  // [chunk][CW/2 pairs] (one batch row)
 
   const int t = threadIdx.x;
   const int team = t / cseg;
@@ -425,7 +381,6 @@ __global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restri
   // chunk i of row b into LDS; every lane then copies its own chunk's pairs
   // into registers
   half2_t xp[B][CW / 2];
-  float xs[B];
   const int64_t cc = c < chunks ? c : 0;
   if constexpr (FMT == FMT_PTQ1) __syncthreads();  // tables ready
 #pragma unroll
@@ -435,14 +390,13 @@ __global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restri
         XRaw<FMT, CW, XD> xr;
         load_x_raw<FMT, CW, XD>(x, b * ldx, i, xr);
         half2_t xp1[CW / 2];
-        const float sum = convert_x_chunk<FMT, CW, XD>(xr, i, xp1);
+        convert_x_chunk<FMT, CW, XD>(xr, i, xp1);
         uint32_t *dst = xlds + (int64_t)i * (CW / 2);
 #pragma unroll
         for (int k = 0; k < CW / 2; k += 4)
           *reinterpret_cast<u32x4 *>(dst + k) = (u32x4){
               __builtin_bit_cast(uint32_t, xp1[k]), __builtin_bit_cast(uint32_t, xp1[k + 1]),
               __builtin_bit_cast(uint32_t, xp1[k + 2]), __builtin_bit_cast(uint32_t, xp1[k + 3])};
-        xlds[(int64_t)chunks * (CW / 2) + i] = __float_as_uint(sum);
       }
     }
     __syncthreads();
@@ -456,7 +410,6 @@ __global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restri
       xp[b][k + 2] = bits_h2(xok ? v[2] : 0u);
       xp[b][k + 3] = bits_h2(xok ? v[3] : 0u);
     }
-    xs[b] = xok ? __uint_as_float(xlds[(int64_t)chunks * (CW / 2) + cc]) : 0.0f;
     __syncthreads();
   }
 
@@ -490,7 +443,7 @@ __global__ __launch_bounds__(LB) void gemv_kernel(Planes p, const void *__restri
       row += row_step;
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        const float v = seg_sum<SEG>(ok ? s * (part[b] - xs[b]) : 0.0f);
+        const float v = seg_sum<SEG>(ok ? s * part[b] : 0.0f);
         if ((t & (SEG - 1)) == SEG - 1) red[(d * B + b) * NSEG + seg] = v;
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -587,7 +540,7 @@ static hipError_t gemv_launch(const Planes &p, const void *x, int64_t batch, int
                               int64_t ldy, int chunks, int cseg, int teams, int threads,
                               hipStream_t st) {
   auto kern = gemv_kernel<FMT, CW, B, D, XD, LB, SEG>;
-  const size_t lds = (size_t)chunks * (CW / 2 + 1) * 4;
+  const size_t lds = (size_t)chunks * (CW / 2) * 4;
   const int64_t npass = (p.n + teams - 1) / teams;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds) != hipSuccess ||

@@ -53,22 +53,6 @@ __device__ __forceinline__ half4_t h4(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(half4_t, (u32x2){a, b});
 }
 
-// Pair of codes (digit i of both bytes) -> pair of binary16 trits, exactly:
-// (P & mask_i) | 0x6400_6400 is 1024 + 4^i * code in each half, and
-// fma(v, 4^-i, -(1024 * 4^-i + 1)) = code - 1.
-template <int I>
-__device__ __forceinline__ uint32_t trit_pair(uint32_t p, uint32_t magic_v) {
-  constexpr uint32_t mask = 0x00030003u << (2 * I);
-  constexpr float inv = I == 0 ? 1.0f : I == 1 ? 0.25f : I == 2 ? 0.0625f : I == 3 ? 0.015625f
-                                                                                   : 0.00390625f;
-  constexpr float neg = I == 0 ? -1025.0f : I == 1 ? -257.0f : I == 2 ? -65.0f : I == 3 ? -17.0f
-                                                                                        : -5.0f;
-  const half2_t t = h2((p & mask) | magic_v);
-  const half2_t m = {(_Float16)inv, (_Float16)inv};
-  const half2_t c = {(_Float16)neg, (_Float16)neg};
-  return u32(__builtin_elementwise_fma(t, m, c));
-}
-
 // One lane's view of a chunk as loaded: the 8-byte window holding its six
 // base bytes, its group's high byte and scale bits.
 struct ChunkRaw {

@@ -12,7 +12,7 @@ namespace tq {
 
 __device__ __forceinline__ half2_t bits_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 
-// The first products of four code classes, a[c] = t[c].lo*x[c].lo +
+// The first products of the four accumulators, a[c] = t[c].lo*x[c].lo +
 // t[c].hi*x[c].hi, each from a zero accumulator (three-operand form; the
 // compiler only emits the two-operand form, whose accumulator is tied to the
 // destination).  A dot product's result may be read by another vector
@@ -31,6 +31,29 @@ __device__ __forceinline__ void dot2_first4(const uint32_t (&t)[8], const half2_
 
 // cache policy of a streaming (read-once) buffer load
 constexpr int CPOL_NT = 2;
+
+// Codes of one 16-weight dword as exact binary16 pairs.  Masked with
+// 0x33333333, each nibble of the dword holds one code in its low two bits,
+// which as an fp4 (E2M1) number is code/2; the converter with scale 2 turns
+// byte B into the pair (code of nibble 2B, code of nibble 2B+1), i.e. the
+// codes 0..3 as normal binary16 values.  The even codes (weights 4B, 4B+2)
+// come from the dword itself, the odd ones (4B+1, 4B+3) from it shifted down
+// two bits.  The codes stay normal numbers on purpose: the dot-product
+// instruction keeps a product only down to a fixed absolute step of about
+// 2^-38, so codes placed as binary16 subnormals (code * 2^-24) would lose
+// the low bits of every product with a small activation.
+template <int B>
+__device__ __forceinline__ uint32_t codes_pair(uint32_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 2.0f, B));
+}
+
+// The eight code pairs of dword w, in the order the activation pairs are
+// staged: pairs 0-3 = even weights (4B, 4B+2), pairs 4-7 = odd (4B+1, 4B+3).
+__device__ __forceinline__ void dword_codes(uint32_t w, uint32_t (&t)[8]) {
+  const uint32_t ev = w & 0x33333333u, od = (w >> 2) & 0x33333333u;
+  t[0] = codes_pair<0>(ev); t[1] = codes_pair<1>(ev); t[2] = codes_pair<2>(ev); t[3] = codes_pair<3>(ev);
+  t[4] = codes_pair<0>(od); t[5] = codes_pair<1>(od); t[6] = codes_pair<2>(od); t[7] = codes_pair<3>(od);
+}
 
 // Row layouts the kernel reads.
 //  LAY_PLANES: PQ2_0_G128 row-split planes ([ninfer-skill] §3): a row's codes
@@ -163,8 +186,7 @@ __device__ __forceinline__ float rows8_sum(const float (&v)[D], int lane, int &r
 // sends thousands of requests to the same few L2 lines.  The first NB waves
 // ("staging" waves) stage it into LDS as binary16 pairs in the order the
 // decoder consumes them, lane-major so that every lane later reads its own
-// pairs with conflict-free 16-byte LDS reads, together with the sum of every
-// lane piece.  The other waves request their first D weight rows as soon
+// pairs with conflict-free 16-byte LDS reads.  The other waves request their first D weight rows as soon
 // as the activations have arrived, so the weight stream runs while the
 // staging waves work; the staging waves request theirs once the staging is
 // done (a wave whose loads fill the compute unit's memory queue stalls at
@@ -196,12 +218,12 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   constexpr bool HEAD = MODE == MODE_HEAD;
   constexpr int NB = 4 * A + BQ;  // 1024-element blocks in a row = 16-weight dwords per lane
   constexpr int NP = A + BQ;      // pieces per lane
-  // Activation pairs: dword s of lane l (16 weights, pairs (e, e+8)) is held
-  // by quads (2s)*64 + l (pairs 0-3) and (2s+1)*64 + l (pairs 4-7).  Dword s
+  // Activation pairs: dword s of lane l (16 weights, pairs (4B, 4B+2) and
+  // (4B+1, 4B+3) as dword_codes orders them) is held by quads (2s)*64 + l
+  // (pairs 0-3) and (2s+1)*64 + l (pairs 4-7).  Dword s
   // of lane l is natural 16-element chunk 256i + 4l + d for s = 4i + d < 4A
   // (a kilobyte piece) and 256A + 64j + l for s = 4A + j (a 256-byte piece).
   __shared__ __attribute__((aligned(16))) u32x4 xq[NB * 128];
-  __shared__ float xsum[NP * 64];  // [piece][lane]: sum of the piece's binary16 activations
   __shared__ uint32_t staged;      // staging waves done
   __shared__ uint32_t sq_posted;   // HEAD: staging waves that posted their sum of squares
   __shared__ float sq_part[HEAD ? WPG : 1];
@@ -438,15 +460,13 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
         for (int m = 0; m < 8; ++m)
           h[m] = (uint32_t)f32_to_f16(v[2 * m]) | ((uint32_t)f32_to_f16(v[2 * m + 1]) << 16);
       }
-      // pairs (e, e+8) of the chunk and their sum
+      // pairs of the chunk in decode order: (4B, 4B+2) then (4B+1, 4B+3)
       uint32_t pr[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pr[e] = __builtin_amdgcn_perm(h[4 + e / 2], h[e / 2], (e & 1) ? 0x07060302u : 0x05040100u);
-      float sum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sum = __builtin_amdgcn_fdot2(bits_h2(pr[e]), bits_h2(0x3C003C00u), sum, false);
+      for (int b = 0; b < 4; ++b) {
+        pr[b] = __builtin_amdgcn_perm(h[2 * b + 1], h[2 * b], 0x05040100u);
+        pr[4 + b] = __builtin_amdgcn_perm(h[2 * b + 1], h[2 * b], 0x07060302u);
+      }
       const int c = FUSED ? (wave + WPG * i) * 64 + lane : (int)threadIdx.x + 64 * WPG * i;
       int s, l;
       if (c < 256 * A) {
@@ -458,17 +478,6 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
       }
       xq[(2 * s) * 64 + l] = (u32x4){pr[0], pr[1], pr[2], pr[3]};
       xq[(2 * s + 1) * 64 + l] = (u32x4){pr[4], pr[5], pr[6], pr[7]};
-      // a kilobyte piece is four consecutive chunks, held by the four lanes
-      // of a DPP quad (chunk index = lane index mod 4): sum them there
-      float qs = sum + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                           __builtin_bit_cast(int, sum), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
-      qs += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                __builtin_bit_cast(int, qs), 0x4E, 0xF, 0xF, false));            // quad_perm 2,3,0,1
-      if (c < 256 * A) {
-        if ((c & 3) == 0) xsum[(c >> 8) * 64 + l] = qs;
-      } else {
-        xsum[(A + ((c - 256 * A) >> 6)) * 64 + l] = sum;
-      }
     }
     // publish: the wave's LDS writes complete before the count (LDS
     // operations only: a release fence would also wait for the global loads)
@@ -493,10 +502,9 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
     asm volatile("" ::: "memory");
   }
 
-  // ---- 4. the lane's activation pairs and piece sums (read before the
-  // staging waves request their rows, which may stall at issue)
+  // ---- 4. the lane's activation pairs (read before the staging waves
+  // request their rows, which may stall at issue)
   half2_t xp[NB][8];
-  float xs[NP];
 #pragma unroll
   for (int s = 0; s < NB; ++s) {
     const u32x4 a = xq[(2 * s) * 64 + lane], b = xq[(2 * s + 1) * 64 + lane];
@@ -506,10 +514,40 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
       xp[s][4 + k] = bits_h2(b[k]);
     }
   }
-#pragma unroll
-  for (int pc = 0; pc < NP; ++pc) xs[pc] = xsum[pc * 64 + lane];
   __builtin_amdgcn_sched_barrier(0);
   if (stager && !ALL_STAGE) load_first();
+  __builtin_amdgcn_sched_barrier(0);
+
+  // sum over the lane's piece pc of code * x' for code words cw[0..nd-1],
+  // in four accumulators (pair e feeds accumulator e % 4; the first product
+  // of each starts from 0 instead of a zeroed register)
+  auto piece_cx = [&](const uint32_t (&cw)[4], int pc) -> float {
+    const int nd = pc < A ? 4 : 1;
+    const int d0 = pc < A ? 4 * pc : 4 * A + (pc - A);
+    float a[4];
+#pragma unroll
+    for (int q = 0; q < nd; ++q) {
+      uint32_t t[8];
+      dword_codes(cw[q], t);
+      if (q == 0) dot2_first4(t, xp[d0], a);
+#pragma unroll
+      for (int e = q == 0 ? 4 : 0; e < 8; ++e)
+        a[e & 3] = __builtin_amdgcn_fdot2(bits_h2(t[e]), xp[d0 + q][e], a[e & 3], false);
+    }
+    return (a[0] + a[1]) + (a[2] + a[3]);
+  };
+  // The offset of the code (trit = code - 1) is applied per piece as
+  // s * (sum code*x' - xs).  xs is the same computation with every code 1,
+  // the same instructions in the same order on the same activations, so a
+  // piece whose weights are all zero gives cx == xs bit for bit and adds
+  // exactly nothing: rounding error arises only in pieces that hold a
+  // nonzero weight, and an all-zero row is exactly 0 at any scale.
+  float xs[NP];
+  {
+    const uint32_t ones[4] = {0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u};
+#pragma unroll
+    for (int pc = 0; pc < NP; ++pc) xs[pc] = piece_cx(ones, pc);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 5. passes of D rows
@@ -518,30 +556,15 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
     float part[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      // sum over the lane's pieces of s * (sum code*x - sum x); the first
-      // product of each class starts from 0 instead of a zeroed register
+      // sum over the lane's pieces of s * (sum code*x' - xs)
       float acc = 0.0f;
 #pragma unroll
       for (int pc = 0; pc < NP; ++pc) {
         const int nd = pc < A ? 4 : 1;
-        const int d0 = pc < A ? 4 * pc : 4 * A + (pc - A);
-        // codes 0-3 (and 8-11) in place, codes 4-7 (and 12-15) shifted
-        // down a byte: four slot classes, e and e+4 in class e
-        float a[4];
+        uint32_t cw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int q = 0; q < nd; ++q) {
-          const uint32_t w = codes_of(ring[d], pc, q), w8 = w >> 8;
-          const uint32_t t[8] = {w & 0x00030003u, w & 0x000C000Cu, w & 0x00300030u,
-                                 w & 0x00C000C0u, w8 & 0x00030003u, w8 & 0x000C000Cu,
-                                 w8 & 0x00300030u, w8 & 0x00C000C0u};
-          if (q == 0) dot2_first4(t, xp[d0], a);
-#pragma unroll
-          for (int e = q == 0 ? 4 : 0; e < 8; ++e)
-            a[e & 3] = __builtin_amdgcn_fdot2(bits_h2(t[e]), xp[d0 + q][e], a[e & 3], false);
-        }
-        const float cx = a[0] * 16777216.0f + a[1] * 4194304.0f + a[2] * 1048576.0f +
-                         a[3] * 262144.0f;
-        acc += f16_to_f32(scale_of(ring[d], pc)) * (cx - xs[pc]);
+        for (int q = 0; q < nd; ++q) cw[q] = codes_of(ring[d], pc, q);
+        acc += f16_to_f32(scale_of(ring[d], pc)) * (piece_cx(cw, pc) - xs[pc]);
       }
       part[d] = acc;
       // refill the slot with its row of the next pass

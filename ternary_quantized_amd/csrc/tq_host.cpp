@@ -612,4 +612,15 @@ tq_status tq_gemv_g64(const uint8_t *blocks, uint64_t blocks_bytes, int64_t n, i
                        "tq_gemv_g64");
 }
 
+tq_status tq_stream_read(const void *src, uint64_t bytes, uint32_t *sink, void *stream) {
+  if (!src || !sink) return fail(TQ_ERR_ARG, "src and sink must be non-NULL");
+  if (bytes < 16 || bytes % 16 || bytes > (uint64_t(1) << 40))
+    return fail(TQ_ERR_SHAPE, "bytes=%llu must be a positive multiple of 16 below 2^40",
+                (unsigned long long)bytes);
+  if (!aligned(src, 16) || !aligned(sink, 4))
+    return fail(TQ_ERR_ALIGN, "src must be 16-byte and sink 4-byte aligned");
+  return device_status(tq::launch_stream_read(src, bytes, sink, (hipStream_t)stream),
+                       "tq_stream_read");
+}
+
 }  // extern "C"

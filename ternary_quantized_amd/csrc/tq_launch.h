@@ -80,6 +80,10 @@ hipError_t launch_head_argmax(const Planes &p, const void *x, int x_dtype, const
                               float eps, const uint16_t *signs, float *logits,
                               unsigned long long *work, int32_t *token, hipStream_t st);
 
+// Plain streaming read of `bytes` (a multiple of 16) from src: the
+// bandwidth reference the GEMVs are measured beside.
+hipError_t launch_stream_read(const void *src, uint64_t bytes, uint32_t *sink, hipStream_t st);
+
 hipError_t launch_decode(const Planes &p, const int32_t *rows, int64_t count,
                          int8_t *values, uint16_t *scale_bits, int64_t k_pad,
                          hipStream_t stream);

@@ -165,3 +165,14 @@ def test_device_entry_validation_without_gpu():
     # a validation failure leaves a message
     assert L.tq_decode_rowsplit(DEV, pb, 141, 64, 1024, DEV, 1, DEV, DEV, None) == 2
     assert b"unknown numeric format" in L.tq_last_error()
+
+
+def test_stream_read_validation_without_gpu():
+    L = tq.lib()
+    assert L.tq_stream_read(None, 1024, DEV, None) == 1
+    assert L.tq_stream_read(DEV, 1024, None, None) == 1
+    assert L.tq_stream_read(DEV, 0, DEV, None) == 5
+    assert L.tq_stream_read(DEV, 1000, DEV, None) == 5
+    assert L.tq_stream_read(DEV, 1 << 41, DEV, None) == 5
+    assert L.tq_stream_read(DEV + 8, 1024, DEV, None) == 4
+    assert L.tq_stream_read(DEV, 1024, DEV + 2, None) == 4

@@ -1,0 +1,183 @@
+"""GPU parity of the batch-1 products on the inputs where a code-offset dot
+product is weakest: large (unit and above) scales, rows that are almost or
+entirely zero, single weights on the smallest activations, and small or
+mixed-magnitude activations.
+
+The batch-1 products take [gguf-explainer] §4.4's offset identity,
+s * sum (code - 1) x = s * (sum code*x - sum x), per lane piece.  Both sums
+run over every weight of the piece, zero weights included, so unless the
+activation sum cancels the zero weights' share exactly, its rounding adds an
+error that grows with s * sum |x| and not with sum |w x|.  The bar is the
+stated one, per output:
+    |gpu - oracle| <= 1e-3 * sum_j |w_j x'_j| + 1e-5,
+and an all-zero row must come out exactly 0 whatever its scales.
+
+Every batch-1 entry point that runs this arithmetic is covered: the GEMV on
+a rotated input, the one-launch decode step (transform inside), the
+one-launch output head (RMSNorm and transform inside), and the GEMV over the
+expanded G64 block stream.
+"""
+
+import numpy as np
+import pytest
+
+import ternary_quantized_amd as tq
+import synth
+from oracle import head as Hd, projection as P, q2g64, transform as T
+from gpu_util import assert_within, dev, say, signs_dev, x_dev, x_f64
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+FMT = "PQ2_0_G128"
+N = 2400
+F16_ONE = 0x3C00
+
+
+def f16_bits(v):
+    return np.asarray(v, np.float64).astype(np.float16).view(np.uint16)
+
+
+def hard_rows(rng, n, k, xrot):
+    """Trits and scale bits of rows of six kinds (row r has kind r % 6):
+    0 all zero at scale 1; 1 all zero at scales up to 1000; 2 one weight in a
+    hundred nonzero, unit scales; 3 one +-1 on one of the 16 smallest |x'|,
+    unit scales; 4 one +-1 anywhere, unit scales; 5 one weight in a thousand,
+    scales exp(N(0, 0.5)).  Returns (trits, scale_bits, zero_rows)."""
+    g = synth.groups_of(k)
+    trits = np.zeros((n, k), np.int8)
+    sb = np.full((n, g), F16_ONE, np.uint16)
+    small = np.argsort(np.abs(xrot))[:16]
+    zero_rows = []
+    for r in range(n):
+        kind = r % 6
+        if kind == 0:
+            zero_rows.append(r)
+        elif kind == 1:
+            sb[r] = f16_bits(rng.choice([1.0, 8.0, 64.0, 1000.0], g))
+            zero_rows.append(r)
+        elif kind == 2:
+            cols = rng.choice(k, k // 100, replace=False)
+            trits[r, cols] = rng.choice(np.array([-1, 1], np.int8), cols.size)
+        elif kind == 3:
+            trits[r, small[r % 16]] = 1 if (r // 6) % 2 else -1
+        elif kind == 4:
+            trits[r, rng.integers(0, k)] = rng.choice(np.array([-1, 1], np.int8))
+        else:
+            cols = rng.choice(k, max(1, k // 1000), replace=False)
+            trits[r, cols] = rng.choice(np.array([-1, 1], np.int8), cols.size)
+            sb[r] = f16_bits(rng.lognormal(0.0, 0.5, g))
+    return trits, sb, np.array(zero_rows)
+
+
+def row2d(a):
+    """A [1, k] array with real strides (a numpy newaxis view has a zero
+    stride on the new axis, which would reach the library as ldx = 0)."""
+    out = np.empty((1, a.size), a.dtype)
+    out[0] = a
+    return out
+
+
+def activation(rng, k, kind):
+    """float32 row: N(0,1); N(0,1) * 1e-3; or N(0,1) with every other
+    1024-element block scaled by 1e-4 (mixed magnitudes)."""
+    x = rng.standard_normal(k).astype(np.float32)
+    if kind == "small":
+        x *= np.float32(1e-3)
+    elif kind == "mixed":
+        for b in range(1, k // 1024, 2):
+            x[1024 * b:1024 * (b + 1)] *= np.float32(1e-4)
+    return x
+
+
+def check_rows(got, payload, k, xrot64, zero_rows, what):
+    expect, bound = P.project_payload(FMT, N, k, payload, xrot64)
+    assert_within(got, expect[0], bound[0], what)
+    z = got[zero_rows]
+    assert np.all(z == 0.0), "%s: all-zero rows must give exactly 0 (got max |y| %r)" % (
+        what, float(np.abs(z).max()))
+
+
+KS = [5120, 11264]
+XKINDS = ["normal", "small", "mixed"]
+
+
+@pytest.mark.parametrize("k", KS)
+@pytest.mark.parametrize("xkind", XKINDS)
+def test_gemv_rowsplit_hard_rows(k, xkind):
+    rng = np.random.default_rng(k + len(xkind))
+    xrot = activation(rng, k, xkind).astype(np.float16)  # the rotated input as binary16
+    xrot64 = xrot.astype(np.float64)
+    trits, sb, zero_rows = hard_rows(rng, N, k, xrot64)
+    payload = tq.pack_rowsplit(FMT, trits, sb)
+    say("gemv hard rows k=%d x=%s" % (k, xkind))
+    y = tq.gemv_rowsplit(dev(torch, payload), FMT, N, k, dev(torch, row2d(xrot)))
+    torch.cuda.synchronize()
+    check_rows(y.cpu().numpy()[0].astype(np.float64), payload, k, xrot64[None, :], zero_rows,
+               "gemv k=%d %s" % (k, xkind))
+
+
+@pytest.mark.parametrize("k", KS)
+@pytest.mark.parametrize("xkind", XKINDS)
+def test_rotated_gemv_hard_rows(k, xkind):
+    rng = np.random.default_rng(2 * k + len(xkind))
+    xb = synth.f32_to_bf16_bits(row2d(activation(rng, k, xkind)))
+    sbits = synth.sign_bits(rng, k)
+    xrot64 = T.forward(x_f64(xb, "bf16"), T.bf16_bits_to_f64(sbits))
+    trits, sb, zero_rows = hard_rows(rng, N, k, xrot64[0])
+    payload = tq.pack_rowsplit(FMT, trits, sb)
+    say("rotated gemv hard rows k=%d x=%s" % (k, xkind))
+    y = tq.rotated_gemv_rowsplit(dev(torch, payload), FMT, N, k, x_dev(torch, xb, "bf16"),
+                                 signs_dev(torch, sbits))
+    torch.cuda.synchronize()
+    check_rows(y.cpu().numpy()[0].astype(np.float64), payload, k, xrot64, zero_rows,
+               "rotated k=%d %s" % (k, xkind))
+
+
+@pytest.mark.parametrize("k", KS)
+@pytest.mark.parametrize("xkind", XKINDS)
+def test_head_hard_rows(k, xkind):
+    rng = np.random.default_rng(3 * k + len(xkind))
+    xb = synth.f32_to_bf16_bits(row2d(activation(rng, k, xkind)))
+    sbits = synth.sign_bits(rng, k)
+    gbits = synth.norm_weight_bits(rng, k)
+    eps = 1e-6
+    xrot64 = T.forward(Hd.rmsnorm(x_f64(xb, "bf16"), T.bf16_bits_to_f64(gbits), eps),
+                       T.bf16_bits_to_f64(sbits))
+    trits, sb, zero_rows = hard_rows(rng, N, k, xrot64[0])
+    payload = tq.pack_rowsplit(FMT, trits, sb)
+    say("head hard rows k=%d x=%s" % (k, xkind))
+    work = torch.zeros(2, dtype=torch.int64, device="cuda")
+    logits = torch.empty(N, dtype=torch.float32, device="cuda")
+    gd = dev(torch, gbits.view(np.int16)).view(torch.bfloat16)
+    tok = tq.head_argmax(dev(torch, payload), FMT, N, k, x_dev(torch, xb, "bf16"), gd, eps,
+                         signs_dev(torch, sbits), work, logits=logits)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy().astype(np.float64)
+    logits_o, bound, _ = Hd.head(FMT, N, k, payload, x_f64(xb, "bf16"), T.bf16_bits_to_f64(gbits),
+                                 eps, T.bf16_bits_to_f64(sbits))
+    assert_within(lg, logits_o[0], bound[0], "head k=%d %s" % (k, xkind))
+    assert np.all(lg[zero_rows] == 0.0)
+    t = int(tok.item())
+    assert t == int(np.flatnonzero(lg == lg.max())[0])
+
+
+@pytest.mark.parametrize("k", KS)
+@pytest.mark.parametrize("xkind", XKINDS)
+def test_gemv_g64_hard_rows(k, xkind):
+    rng = np.random.default_rng(4 * k + len(xkind))
+    xrot = activation(rng, k, xkind).astype(np.float16)
+    xrot64 = xrot.astype(np.float64)
+    trits, sb, zero_rows = hard_rows(rng, N, k, xrot64)
+    payload = tq.pack_rowsplit(FMT, trits, sb)
+    say("g64 gemv hard rows k=%d x=%s" % (k, xkind))
+    blocks = tq.expand_g64(dev(torch, payload), FMT, N, k)
+    y = tq.gemv_g64(blocks, N, k, dev(torch, row2d(xrot)))
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()[0].astype(np.float64)
+    stream = q2g64.expand(FMT, N, k, payload)
+    expect = q2g64.project(stream, N, k, xrot64[None, :])[0]
+    w = q2g64.dequantize(stream, N, k)
+    bound = P.REL * (np.abs(w[:, :k]) @ np.abs(xrot64)) + P.ABS
+    assert_within(got, expect, bound, "g64 k=%d %s" % (k, xkind))
+    assert np.all(got[zero_rows] == 0.0)
