@@ -114,7 +114,9 @@ tq_status tq_pack_rowsplit(int32_t format, int64_t n, int64_t k,
                            const uint16_t *host_scale_bits,
                            uint8_t *host_payload, uint64_t payload_bytes);
 
-/* Host unpacker (inverse of tq_pack_rowsplit): host_values int8 [n][k_pad]
+/* Host unpacker (inverse of tq_pack_rowsplit), by the same plane addressing
+ * ([ninfer-skill] §3) and code rules ([gguf-explainer] §4.3 for PQ2_0: value
+ * code-1; the radix-3 convention above for PTQ1_0): host_values int8 [n][k_pad]
  * receives code-1 for PQ2_0 (so -1..2) and the decoded digit-1 for PTQ1_0;
  * host_scale_bits [n][groups_per_row] receives the stored binary16 bits.
  * *host_bad_codes (may be NULL) receives the number of stored codes that are
@@ -264,7 +266,10 @@ tq_status tq_hadamard_signed_grouped(const void *x, int32_t x_dtype, int64_t row
                                      int32_t head_dim, const uint16_t *signs_bf16, void *y,
                                      int32_t y_dtype, int64_t ldy, void *stream);
 
-/* Decode GEMV: y[b][n] = sum_g s[n][g] * sum_{j in g} t[n][j] * xrot[b][j]
+/* Decode GEMV ([ninfer-v3] §8: a projection multiplies the stored matrix by
+ * the transformed input; [gguf-explainer] §4.3-§4.4: value (code-1)*d per
+ * group, dot product with the activations):
+ *   y[b][n] = sum_g s[n][g] * sum_{j in g} t[n][j] * xrot[b][j]
  * for b < batch, n < N, over the row-split payload (`payload`, exactly
  * payload_bytes bytes, 256-byte aligned).  xrot: already-rotated
  * activations, x_dtype F32, BF16 or F16, row-major [batch][ldx]; the kernel
@@ -311,7 +316,8 @@ tq_status tq_rotated_gemv_rowsplit(const uint8_t *payload, uint64_t payload_byte
  * work: two uint64 words of device memory, 16-byte aligned, owned by the
  * caller, zero before the first call; every call leaves them zero again.
  * Calls that share a work buffer must not run concurrently.  token: one
- * device int32 (-1 if no logit is ordered, i.e. all are NaN).
+ * device int32.  A NaN logit is never chosen (it orders below every number,
+ * -inf included); if every logit is NaN the token is -1.
  * Requirements: k % 1024 == 0, n < 2^30 (TQ_ERR_SHAPE); alignment as above
  * (TQ_ERR_ALIGN).  Covered: PQ2_0_G128 with k <= 11264 (the decode GEMV's
  * batch-1 kernel); other valid requests return TQ_ERR_UNSUPPORTED with
@@ -332,7 +338,10 @@ tq_status tq_rotated_gemv_rowsplit_grouped(const uint8_t *payload, uint64_t payl
                                            const uint16_t *signs_bf16, float *y, int64_t ldy,
                                            void *stream);
 
-/* Prefill GEMM: Y[m][n] = sum_g s[n][g] * sum_{j in g} t[n][j] * X[m][j]
+/* Prefill GEMM ([tensorsharp] §4.4: every low-bit projection of the
+ * network, prefill included, takes the rotated input; [gguf-explainer] §4.3
+ * code rule):
+ *   Y[m][n] = sum_g s[n][g] * sum_{j in g} t[n][j] * X[m][j]
  * for m < M rows of rotated activations X (x_dtype TQ_F16 or TQ_BF16,
  * row-major [M][ldx], 16-byte aligned, ldx a multiple of 8) against a
  * PQ2_0_G128 or PTQ1_0_G128 payload, on the matrix cores.  Each weight is
@@ -359,7 +368,10 @@ tq_status tq_embed_rows_inverse(const uint8_t *payload, uint64_t payload_bytes,
                                 const uint16_t *signs_bf16, float *out,
                                 int64_t ldo, int32_t *err_word, void *stream);
 
-/* Decode hook (for bit-exact checks): for each of `count` row indices in
+/* Decode hook (for bit-exact checks of the device unpack against the code
+ * rules: [gguf-explainer] §4.3 for PQ2_0, the radix-3 convention above for
+ * PTQ1_0; planes addressed as in [ninfer-skill] §3): for each of `count` row
+ * indices in
  * `rows` (device int32, each in [0, n); others give zero output), write the
  * decoded values code-1 / digit-1 to values [count][k_pad] (int8) and the
  * stored scale bits to scale_bits [count][groups_per_row] (uint16). */

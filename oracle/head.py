@@ -12,7 +12,8 @@ Readings (the pages name the steps but not their formulas):
   eps an argument (the plain RMSNorm; a model that stores g as an offset from
   one passes 1 + g);
 * the transform is the forward signed transform of the projection inputs;
-* greedy choice: the lowest index among the largest logits.
+* greedy choice: the lowest index among the largest logits; NaN logits are
+  never chosen, and a row of NaN logits gives -1.
 """
 
 import numpy as np
@@ -29,9 +30,20 @@ def rmsnorm(x, g, eps):
 
 
 def greedy(logits):
-    """Index of the largest logit per row; the lowest such index on a tie."""
+    """Index of the largest logit per row; the lowest such index on a tie.
+    A NaN logit is not a number to compare, so it is never chosen; a row whose
+    logits are all NaN has no choice, reported as -1 (a reading: the pages do
+    not say)."""
     logits = np.atleast_2d(np.asarray(logits, dtype=np.float64))
-    return np.array([int(np.flatnonzero(row == row.max())[0]) for row in logits])
+    out = []
+    for row in logits:
+        ok = ~np.isnan(row)
+        if not ok.any():
+            out.append(-1)
+            continue
+        best = row[ok].max()
+        out.append(int(np.flatnonzero(ok & (row == best))[0]))
+    return np.array(out)
 
 
 def head(fmt, n, k, payload, x, g, eps, signs):

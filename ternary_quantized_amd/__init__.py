@@ -19,7 +19,9 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libtq.so")
+# TQ_LIBRARY names another build of the same C ABI (the host-only sanitizer
+# build); by default the in-tree libtq.so.
+LIB_PATH = os.environ.get("TQ_LIBRARY") or os.path.join(HERE, "libtq.so")
 
 PQ2_0_G128 = 142
 PTQ1_0_G128 = 143

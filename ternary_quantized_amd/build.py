@@ -62,5 +62,30 @@ def build(verbose=False):
     return LIB
 
 
+# The host-only build: the C ABI's host sources (validation, geometry, host
+# packer, container parser) under AddressSanitizer and
+# UndefinedBehaviorSanitizer, linked with tq_host_only.cpp in place of the
+# kernels.  It needs no GPU; the CPU tests run against it with
+#   TQ_LIBRARY=<this .so> LD_PRELOAD="<libasan.so> <libubsan.so>"
+#   ASAN_OPTIONS=detect_leaks=0 python -m pytest tests -m "not gpu"
+SANITIZE_LIB = os.path.join(BUILD, "libtq_host_sanitize.so")
+SANITIZE_SOURCES = ["tq_host.cpp", "tq_container.cpp", "tq_host_only.cpp"]
+
+
+def build_sanitize():
+    os.makedirs(BUILD, exist_ok=True)
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["g++", "-std=c++17", "-g", "-O1", "-fPIC", "-shared", "-Wall",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(rocm, "include"),
+           *[os.path.join(CSRC, f) for f in SANITIZE_SOURCES],
+           "-L" + os.path.join(rocm, "lib"), "-lamdhip64", "-o", SANITIZE_LIB]
+    _run(cmd)
+    return SANITIZE_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitize())
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -472,13 +472,6 @@ static hipError_t gemv_wave_dt(const Planes &p, const void *x, int xd, const uin
   return gemv_wave_go<LAY_PLANES, A, BQ, DT_F16, FUSED>(p, x, signs, y, st, sa);
 }
 
-// k = 1024*m: pieces A = m/4 kilobytes + BQ = m%4 blocks; m <= 17 for the
-// GEMV alone, m <= 11 with the transform fused in.
-static bool gemv_wave_fits(const Planes &p, bool fused) {
-  return p.fmt == FMT_PQ2 && p.k % 1024 == 0 && p.k / 1024 >= 1 &&
-         p.k / 1024 <= (fused ? 11 : 17) && p.n < (int64_t(1) << 30);
-}
-
 template <bool FUSED>
 static hipError_t gemv_wave(const Planes &p, const void *x, int xd, const uint16_t *signs, float *y,
                             hipStream_t st, const StepArgs &sa = StepArgs{}) {
@@ -593,8 +586,6 @@ static hipError_t gemv_b1(const Planes &p, const void *x, int xd, int64_t ldx, f
   return gemv_go<FMT, CW, 1, 4>(p, x, xd, 1, ldx, y, ldy, st);
 }
 
-int64_t gemv_max_k(int fmt) { return fmt == FMT_PQ2 ? 64 * 1024 : 32 * 1024; }
-
 // Lane chunk (CW weights), batch tile (B) and rows per thread (P) by batch:
 // smaller chunks and fewer rows at larger batch keep the activation pairs
 // (B * CW / 2 registers) and partial sums in registers without spilling.
@@ -632,10 +623,6 @@ hipError_t launch_gemv(const Planes &p, const void *x, int xd, int64_t batch, in
   if (batch <= 4) return gemv_go<FMT_PQ2, 32, 4, 2>(p, x, xd, batch, ldx, y, ldy, st);
   if (wide16) return gemv_go<FMT_PQ2, 32, 8, 1>(p, x, xd, batch, ldx, y, ldy, st);
   return gemv_go<FMT_PQ2, 16, 8, 2>(p, x, xd, batch, ldx, y, ldy, st);
-}
-
-bool rotated_gemv_fused(const Planes &p, int64_t batch) {
-  return batch == 1 && gemv_wave_fits(p, true);
 }
 
 hipError_t launch_rotated_gemv(const Planes &p, const void *x, int xd, const uint16_t *signs,

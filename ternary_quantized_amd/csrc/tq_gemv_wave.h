@@ -100,11 +100,14 @@ __device__ __forceinline__ int head_src(int j, int tiles, int groups, int head_d
 // Order-preserving 64-bit key of (logit v, row i): the float's bits mapped
 // so that unsigned order is numeric order (-0 is taken as +0), above the
 // complement of the index, so that the maximum key is the largest logit
-// with the lowest index.
+// with the lowest index.  A NaN logit is not ordered: its key is 0, the key
+// of "no row", which every number (-inf included) beats, so a NaN is never
+// the token and a head of NaN logits gives -1.
 __device__ __forceinline__ unsigned long long greedy_key(float v, uint32_t i) {
   const uint32_t u = __float_as_uint(v + 0.0f);
   const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((unsigned long long)o << 32) | (0xFFFFFFFFu - i);
+  const unsigned long long key = ((unsigned long long)o << 32) | (0xFFFFFFFFu - i);
+  return v == v ? key : 0ull;
 }
 
 // ---------------------------------------------------------------------------

@@ -522,28 +522,48 @@ tq_status tq_planes_to_blocks(const uint8_t *payload, uint64_t payload_bytes, in
                    "tq_planes_to_blocks");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the two entry points of the one-launch head.
+tq_status check_head(const uint8_t *payload, uint64_t payload_bytes, int32_t format, int64_t n,
+                     int64_t k, const void *x, int32_t x_dtype, const uint16_t *norm_bf16,
+                     float eps, const uint16_t *signs_bf16, const float *logits,
+                     const int32_t *token, tq_geometry *g, tq::Planes *p) {
+  tq_status st = check_device_payload(payload, payload_bytes, format, n, k, g, p);
+  if (st != TQ_OK) return st;
+  if (k % 1024) return fail(TQ_ERR_SHAPE, "k=%lld: the head step needs k %% 1024 == 0", (long long)k);
+  if (n >= (int64_t(1) << 30)) return fail(TQ_ERR_SHAPE, "n=%lld must be below 2^30", (long long)n);
+  if (!dtype_ok(x_dtype)) return fail(TQ_ERR_ARG, "x_dtype must be TQ_F32, TQ_BF16 or TQ_F16");
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(TQ_ERR_ARG, "eps must be finite and >= 0");
+  if (!x || !norm_bf16 || !token) return fail(TQ_ERR_ARG, "x, norm_bf16 and token must be non-NULL");
+  if ((st = check_signs(signs_bf16)) != TQ_OK) return st;
+  if (!aligned(x, 16) || !aligned(norm_bf16, 16))
+    return fail(TQ_ERR_ALIGN, "x and norm_bf16 must be 16-byte aligned");
+  if (!aligned(token, 4) || (logits && !aligned(logits, 4)))
+    return fail(TQ_ERR_ALIGN, "token and logits must be 4-byte aligned");
+  if (format != TQ_PQ2_0_G128 || k > 11 * 1024)
+    return fail(TQ_ERR_UNSUPPORTED, "the one-launch head covers PQ2_0_G128 with k <= 11264; "
+                "use tq_hadamard_signed then tq_gemv_rowsplit");
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 tq_status tq_head_argmax(const uint8_t *payload, uint64_t payload_bytes, int32_t format,
                          int64_t n, int64_t k, const void *x, int32_t x_dtype,
                          const uint16_t *norm_bf16, float eps, const uint16_t *signs_bf16,
                          float *logits, uint64_t *work, int32_t *token, void *stream) {
   tq_geometry g;
   tq::Planes p;
-  tq_status st = check_device_payload(payload, payload_bytes, format, n, k, &g, &p);
+  tq_status st = check_head(payload, payload_bytes, format, n, k, x, x_dtype, norm_bf16, eps,
+                            signs_bf16, logits, token, &g, &p);
   if (st != TQ_OK) return st;
-  if (k % 1024) return fail(TQ_ERR_SHAPE, "k=%lld: the head step needs k %% 1024 == 0", (long long)k);
-  if (n >= (int64_t(1) << 30)) return fail(TQ_ERR_SHAPE, "n=%lld must be below 2^30", (long long)n);
-  if (!dtype_ok(x_dtype)) return fail(TQ_ERR_ARG, "x_dtype must be TQ_F32, TQ_BF16 or TQ_F16");
-  if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(TQ_ERR_ARG, "eps must be finite and >= 0");
-  if (!x || !norm_bf16 || !work || !token)
-    return fail(TQ_ERR_ARG, "x, norm_bf16, work and token must be non-NULL");
-  if ((st = check_signs(signs_bf16)) != TQ_OK) return st;
-  if (!aligned(x, 16) || !aligned(norm_bf16, 16))
-    return fail(TQ_ERR_ALIGN, "x and norm_bf16 must be 16-byte aligned");
-  if (!aligned(work, 16) || !aligned(token, 4) || (logits && !aligned(logits, 4)))
-    return fail(TQ_ERR_ALIGN, "work must be 16-byte aligned, token and logits 4-byte aligned");
-  if (format != TQ_PQ2_0_G128 || k > 11 * 1024)
-    return fail(TQ_ERR_UNSUPPORTED, "the one-launch head covers PQ2_0_G128 with k <= 11264; "
-                "use tq_hadamard_signed then tq_gemv_rowsplit");
+  if (!work) return fail(TQ_ERR_ARG, "work must be non-NULL");
+  if (!aligned(work, 16)) return fail(TQ_ERR_ALIGN, "work must be 16-byte aligned");
   return device_status(tq::launch_head_argmax(p, x, x_dtype, norm_bf16, eps, signs_bf16, logits,
                                               reinterpret_cast<unsigned long long *>(work), token,
                                               (hipStream_t)stream),

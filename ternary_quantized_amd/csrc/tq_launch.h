@@ -33,7 +33,15 @@ hipError_t launch_gemm(const Planes &p, const uint16_t *x, int x_dtype,
                        int64_t m, int64_t ldx, void *y, int y_dtype,
                        int64_t ldy, hipStream_t stream);
 
-int64_t gemv_max_k(int fmt);
+// Longest rows the decode GEMV accepts (the team kernel's reach).
+inline int64_t gemv_max_k(int fmt) { return fmt == 142 ? 64 * 1024 : 32 * 1024; }
+
+// Shapes of the batch-1 wave kernel: PQ2_0, k = 1024*m with m <= 17 for the
+// GEMV alone and m <= 11 with the transform fused in, n < 2^30.
+inline bool gemv_wave_fits(const Planes &p, bool fused) {
+  return p.fmt == 142 && p.k % 1024 == 0 && p.k / 1024 >= 1 &&
+         p.k / 1024 <= (fused ? 11 : 17) && p.n < (int64_t(1) << 30);
+}
 
 // GEMV on the matrix cores over row-quads (either format, any batch, in
 // passes of up to eight rows): shapes it covers, and the launch.
@@ -44,7 +52,9 @@ hipError_t launch_gemv_quads(const Planes &p, const void *x, int x_dtype, int64_
 // Signed transform fused into the GEMV (one launch): supported shapes, and
 // the launch itself (x unrotated, signs bf16 +-1; tiles > 0 gathers x into
 // the grouped head order of tiles x groups heads of head_dim first).
-bool rotated_gemv_fused(const Planes &p, int64_t batch);
+inline bool rotated_gemv_fused(const Planes &p, int64_t batch) {
+  return batch == 1 && gemv_wave_fits(p, true);
+}
 hipError_t launch_rotated_gemv(const Planes &p, const void *x, int x_dtype,
                                const uint16_t *signs, float *y, hipStream_t st,
                                int tiles = 0, int groups = 0, int head_dim = 0);

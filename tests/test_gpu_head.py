@@ -185,3 +185,41 @@ def test_head_rejects_uncovered_requests():
     with pytest.raises(tq.TQError) as e:
         tq.head_argmax(pd, "PTQ1_0_G128", n, k, x, x, 1e-6, x, work)
     assert e.value.status == 6
+
+
+def test_head_nan_logits_are_never_chosen():
+    """Rows whose logit is NaN (planted through a NaN group scale, outside the
+    formats' finite scales, only to make NaN logits) are never the token, even
+    where the row would otherwise hold the maximum; a hidden row with a NaN
+    makes every logit NaN, and the token is then -1."""
+    rng = np.random.default_rng(31)
+    n, k = 3000, 2048
+    z = rng.standard_normal((1, k))
+    c_star = int(np.argmax(z))
+    z[0, c_star] += 1.0
+    cols = rng.integers(0, k, n)
+    cols[cols == c_star] = (c_star + 1) % k
+    winners = [7, 1500]                      # would tie for the maximum
+    cols[winners] = c_star
+    sb = np.full(n, 0x3C00, np.uint16)
+    sb[7] = 0x7E00                           # NaN scale: row 7's logit is NaN
+    sb[[0, 2999]] = 0x7E00
+    payload = single_trit_head(n, k, cols, sb)
+    sbits = synth.sign_bits(rng, k)
+    x = T.inverse(z, T.bf16_bits_to_f64(sbits)).astype(np.float32)
+    gbits = np.full(k, 0x3F80, np.uint16)
+    say("head NaN logits")
+    pd = dev(torch, payload)
+    tok, lg = run_head(pd, n, k, x, "f32", gbits, 0.0, sbits)
+    assert np.isnan(lg[[0, 7, 2999]]).all() and not np.isnan(np.delete(lg, [0, 7, 2999])).any()
+    assert tok == 1500
+    lo, bound, _ = Hd.head(FMT, n, k, payload, x_f64(x, "f32"), T.bf16_bits_to_f64(gbits), 0.0,
+                           T.bf16_bits_to_f64(sbits))
+    assert int(Hd.greedy(lo)[0]) == 1500
+    ok = ~np.isnan(lo[0])
+    assert_within(lg[ok], lo[0][ok], bound[0][ok], "head logits beside NaN rows")
+    # a NaN in the hidden row: every logit NaN, no token
+    xn = x.copy()
+    xn[0, 5] = np.nan
+    tok, lg = run_head(pd, n, k, xn, "f32", gbits, 0.0, sbits)
+    assert np.isnan(lg).all() and tok == -1

@@ -90,9 +90,10 @@ def test_hadamard_in_place_strided_and_stream():
                          [("bf16", "f16", 0, 3001, 3072, False), ("f32", "f32", 1, 2500, 2048, True),
                           ("f16", "f16", 0, 4099, 1024, True)])
 def test_hadamard_many_rows(xdt, ydt, inverse, rows, k, in_place):
-    """More blocks than the launch has waves: each wave transforms several
-    blocks in turn (its next block requested before the current one is
-    stored), with a ragged last round; in place too."""
+    """Thousands of rows: one wave per 1024-element block, four per
+    workgroup, so the grid ends in a partly filled last workgroup when the
+    block count is not a multiple of four (3001 rows x 3 blocks); in place
+    too."""
     rng = np.random.default_rng(rows + k)
     sbits = synth.sign_bits(rng, k)
     x = rand_x(rng, rows, k, xdt, scale=2.0)

@@ -42,6 +42,14 @@ def test_greedy_lowest_index_on_ties():
     assert list(Hd.greedy([[1.0, 2.0], [9.0, 9.0]])) == [1, 0]
 
 
+def test_greedy_skips_nan_logits():
+    # NaN is never the choice; all-NaN rows have none (-1); -inf still counts
+    nan = np.nan
+    assert list(Hd.greedy([[nan, 1.0, 3.0, nan, 3.0]])) == [2]
+    assert list(Hd.greedy([[nan, -np.inf]])) == [1]
+    assert list(Hd.greedy([[nan, nan], [nan, 0.5]])) == [-1, 1]
+
+
 @pytest.mark.parametrize("fmt", ["PQ2_0_G128", "PTQ1_0_G128"])
 def test_constructed_head(fmt):
     """Row i of W has one trit +1 at column c_i with scale s_i; the hidden row
