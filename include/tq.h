@@ -327,6 +327,22 @@ tq_status tq_head_argmax(const uint8_t *payload, uint64_t payload_bytes, int32_t
                          const uint16_t *norm_bf16, float eps, const uint16_t *signs_bf16,
                          float *logits, uint64_t *work, int32_t *token, void *stream);
 
+/* tq_head_argmax for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation, arguments, requirements and results, without the
+ * `work` argument.  The two work words live in a device global of 16 bytes
+ * per GPU inside the library, held until the process ends; no call
+ * allocates or frees anything.  Every request the one-launch head covers
+ * (n < 2^30, k <= 11264) fits those two words; other requests are rejected
+ * as by tq_head_argmax (TQ_ERR_SHAPE / TQ_ERR_UNSUPPORTED).  Each call
+ * leaves the words zero for the next.  All calls on one GPU share them:
+ * calls that overlap on one GPU (on different streams, or from different
+ * threads) race and must not be issued. */
+tq_status tq_head_argmax_noalloc(const uint8_t *payload, uint64_t payload_bytes, int32_t format,
+                                 int64_t n, int64_t k, const void *x, int32_t x_dtype,
+                                 const uint16_t *norm_bf16, float eps, const uint16_t *signs_bf16,
+                                 float *logits, int32_t *token, void *stream);
+
 /* tq_rotated_gemv_rowsplit with the grouped head order: the signed
  * transform input is x gathered as for tq_hadamard_signed_grouped, i.e.
  * exactly tq_hadamard_signed_grouped (y_dtype F16) then tq_gemv_rowsplit, in

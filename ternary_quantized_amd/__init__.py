@@ -43,7 +43,7 @@ EXPORTS = (
     "tq_rotated_gemv_rowsplit", "tq_blocks_to_planes", "tq_planes_to_blocks",
     "tq_container_parse", "tq_container_object_at", "tq_g64_bytes", "tq_expand_g64",
     "tq_gemv_g64", "tq_head_argmax", "tq_hadamard_signed_grouped",
-    "tq_rotated_gemv_rowsplit_grouped", "tq_stream_read",
+    "tq_rotated_gemv_rowsplit_grouped", "tq_stream_read", "tq_head_argmax_noalloc",
 )
 
 
@@ -105,6 +105,8 @@ def lib():
                                                  _i32, _i32, _i32, _vp, _vp, _i64, _vp],
             "tq_gemv_g64": [_vp, _u64, _i64, _i64, _vp, _i32, _i64, _i64, _vp, _i64, _vp],
             "tq_stream_read": [_vp, _u64, _vp, _vp],
+            "tq_head_argmax_noalloc": [_vp, _u64, _i32, _i64, _i64, _vp, _i32, _vp, ctypes.c_float,
+                                       _vp, _vp, _vp, _vp],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -393,6 +395,24 @@ def head_argmax(payload, fmt, n, k, x, norm, eps, signs, work, logits=None, toke
                                 _fmt(fmt), n, k, x.data_ptr(), _dtype_code(x), norm.data_ptr(),
                                 float(eps), _signs_ptr(signs), lp, work.data_ptr(), token.data_ptr(),
                                 _stream(x.device)))
+    return token
+
+
+def head_argmax_noalloc(payload, fmt, n, k, x, norm, eps, signs, logits=None, token=None):
+    """head_argmax without a work buffer: the work words are the library's
+    own per-GPU device global (calls on one GPU must not overlap).  The token
+    tensor is allocated here when not given; pass `token` (and `logits`) to
+    call without any allocation, e.g. under graph capture."""
+    torch = _torch()
+    for t, name in ((payload, "payload"), (x, "x"), (norm, "norm"), (signs, "signs")):
+        _dev(t, name)
+    if token is None:
+        token = torch.empty(1, dtype=torch.int32, device=x.device)
+    lp = None if logits is None else logits.data_ptr()
+    _check(lib().tq_head_argmax_noalloc(payload.data_ptr(), payload.numel() * payload.element_size(),
+                                        _fmt(fmt), n, k, x.data_ptr(), _dtype_code(x), norm.data_ptr(),
+                                        float(eps), _signs_ptr(signs), lp, token.data_ptr(),
+                                        _stream(x.device)))
     return token
 
 

@@ -8,7 +8,17 @@
 #include "tq_gemv_wave.h"
 #include "tq_launch.h"
 
+#include <mutex>
+
 namespace tq {
+
+// The head's two work words (running maximum key, finished-workgroup count)
+// for tq_head_argmax_noalloc, whose callers cannot allocate device memory:
+// one copy per GPU, held until the process ends.  Device globals start at
+// zero when the code object is loaded, and every launch's last workgroup
+// writes them back to zero, so each call finds them zero.  Calls on one GPU
+// share them: calls that overlap on one GPU race.
+static __device__ __align__(256) unsigned long long scratch[HEAD_SCRATCH_WORDS];
 
 namespace {
 
@@ -43,6 +53,29 @@ hipError_t launch_head_argmax(const Planes &p, const void *x, int x_dtype, const
     case 10: return head_dt<2, 2>(p, x, x_dtype, signs, logits, hd, st);
     default: return head_dt<2, 3>(p, x, x_dtype, signs, logits, hd, st);
   }
+}
+
+// Device address of `scratch` on the current device.  In host code the
+// array's name is only a host-side handle, so its device address is looked
+// up once per device (with that device current) and kept.
+hipError_t head_scratch(unsigned long long **out) {
+  constexpr int MAXDEV = 64;
+  static std::mutex mu;
+  static unsigned long long *addr[MAXDEV] = {nullptr};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAXDEV) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    addr[dev] = static_cast<unsigned long long *>(ptr);
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace tq

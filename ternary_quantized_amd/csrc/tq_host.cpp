@@ -570,6 +570,25 @@ tq_status tq_head_argmax(const uint8_t *payload, uint64_t payload_bytes, int32_t
                        "tq_head_argmax");
 }
 
+tq_status tq_head_argmax_noalloc(const uint8_t *payload, uint64_t payload_bytes, int32_t format,
+                                 int64_t n, int64_t k, const void *x, int32_t x_dtype,
+                                 const uint16_t *norm_bf16, float eps, const uint16_t *signs_bf16,
+                                 float *logits, int32_t *token, void *stream) {
+  tq_geometry g;
+  tq::Planes p;
+  // every request the one-launch head covers (n < 2^30, k <= 11264) needs
+  // the same two work words, so check_head's limits are the scratch's too
+  tq_status st = check_head(payload, payload_bytes, format, n, k, x, x_dtype, norm_bf16, eps,
+                            signs_bf16, logits, token, &g, &p);
+  if (st != TQ_OK) return st;
+  unsigned long long *work = nullptr;
+  if ((st = device_status(tq::head_scratch(&work), "tq_head_argmax_noalloc: scratch address")) != TQ_OK)
+    return st;
+  return device_status(tq::launch_head_argmax(p, x, x_dtype, norm_bf16, eps, signs_bf16, logits,
+                                              work, token, (hipStream_t)stream),
+                       "tq_head_argmax_noalloc");
+}
+
 // 2-bit G64 block stream ([tensorsharp] §4.1 expansion; block rule of
 // [gguf-explainer] §4.3): n rows of k_pad/64 blocks of 18 bytes.
 static uint64_t g64_bytes(const tq_geometry &g) { return g.n * (g.k_pad / 64) * 18; }

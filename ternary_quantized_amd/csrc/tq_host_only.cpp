@@ -32,6 +32,7 @@ hipError_t launch_gemv_g64(const uint8_t *, int64_t, int64_t, const void *, int,
 hipError_t launch_head_argmax(const Planes &, const void *, int, const uint16_t *, float,
                               const uint16_t *, float *, unsigned long long *, int32_t *,
                               hipStream_t) { return none(); }
+hipError_t head_scratch(unsigned long long **) { return none(); }
 hipError_t launch_stream_read(const void *, uint64_t, uint32_t *, hipStream_t) { return none(); }
 hipError_t launch_decode(const Planes &, const int32_t *, int64_t, int8_t *, uint16_t *, int64_t,
                          hipStream_t) { return none(); }

@@ -90,6 +90,12 @@ hipError_t launch_head_argmax(const Planes &p, const void *x, int x_dtype, const
                               float eps, const uint16_t *signs, float *logits,
                               unsigned long long *work, int32_t *token, hipStream_t st);
 
+// tq_head_argmax_noalloc: the head's work words live in a device global of
+// HEAD_SCRATCH_WORDS 64-bit words per GPU (tq_head.hip); head_scratch gives
+// its address on the current device (looked up once per device).
+constexpr int HEAD_SCRATCH_WORDS = 2;
+hipError_t head_scratch(unsigned long long **out);
+
 // Plain streaming read of `bytes` (a multiple of 16) from src: the
 // bandwidth reference the GEMVs are measured beside.
 hipError_t launch_stream_read(const void *src, uint64_t bytes, uint32_t *sink, hipStream_t st);
