@@ -15,7 +15,8 @@ LIB = os.path.join(HERE, "libtq.so")
 BUILD = os.path.join(HERE, "_build")
 
 HIP_SOURCES = ["tq_hadamard.hip", "tq_gemv.hip", "tq_gemv_quads.hip", "tq_gemm.hip",
-               "tq_transcode.hip", "tq_q2g64.hip", "tq_head.hip", "tq_measure.hip"]
+               "tq_transcode.hip", "tq_q2g64.hip", "tq_head.hip", "tq_measure.hip",
+               "tq_gemv_f4.hip"]
 HOST_SOURCES = ["tq_host.cpp", "tq_container.cpp"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 arithmetic.

@@ -22,6 +22,7 @@
 //    reproducible).
 
 #include "tq_device.h"
+#include "tq_gemv_f4.h"
 #include "tq_gemv_wave.h"
 #include "tq_launch.h"
 
@@ -610,6 +611,7 @@ hipError_t launch_gemv(const Planes &p, const void *x, int xd, int64_t batch, in
   // a chunk never spans two groups (64 | 128); wide rows need wider chunks
   const bool wide32 = p.k / 32 > 1024, wide16 = p.k / 16 > 1024;
   if (batch >= 2 && gemv_quads_fits(p)) return launch_gemv_quads(p, x, xd, batch, ldx, y, ldy, st);
+  if (batch <= 1 && gemv_f4_fits(p)) return launch_gemv_f4(p, x, xd, nullptr, y, MODE_GEMV, StepArgs{}, st);
   if (batch <= 1 && gemv_wave_fits(p, false)) return gemv_wave<false>(p, x, xd, nullptr, y, st);
   if (batch <= 1 || (wide32 && batch <= 2)) {
     if (batch <= 1) return gemv_b1<FMT_PQ2, 64>(p, x, xd, ldx, y, ldy, st);
@@ -631,6 +633,7 @@ hipError_t launch_rotated_gemv(const Planes &p, const void *x, int xd, const uin
   sa.tiles = tiles;
   sa.groups = groups;
   sa.head_dim = head_dim;
+  if (gemv_f4_fits(p)) return launch_gemv_f4(p, x, xd, signs, y, MODE_ROT, sa, st);
   return gemv_wave<true>(p, x, xd, signs, y, st, sa);
 }
 

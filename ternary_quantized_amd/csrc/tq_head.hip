@@ -5,6 +5,7 @@
 // reduces the logits to the greedy token (largest logit, lowest index).
 
 #include "tq_device.h"
+#include "tq_gemv_f4.h"
 #include "tq_gemv_wave.h"
 #include "tq_launch.h"
 
@@ -40,6 +41,7 @@ hipError_t launch_head_argmax(const Planes &p, const void *x, int x_dtype, const
   hd.eps = eps;
   hd.work = work;
   hd.token = token;
+  if (gemv_f4_fits(p)) return launch_gemv_f4(p, x, x_dtype, signs, logits, MODE_HEAD, hd, st);
   switch (p.k / 1024) {
     case 1: return head_dt<0, 1>(p, x, x_dtype, signs, logits, hd, st);
     case 2: return head_dt<0, 2>(p, x, x_dtype, signs, logits, hd, st);

@@ -111,8 +111,12 @@ def test_gemv_g64_multi_pass_integer_exact(n, k):
 
 @pytest.mark.parametrize("n,k", [(17408, 5120), (1000, 11264), (513, 2048)])
 def test_gemv_g64_equals_plane_gemv(n, k):
-    """On PQ2_0 data the G64 GEMV reads the same codes and scales in the same
-    order as the plane GEMV, so the two results are bit-identical."""
+    """On PQ2_0 data the G64 GEMV and the plane GEMV read the same codes and
+    scales.  Where the plane GEMV runs the dot-product kernel (matrices under
+    2^29 weights, rows over 8192 weights) both do the same arithmetic in the
+    same order and the results are bit-identical; where it takes the
+    matrix-core kernel, whose sums are grouped differently, both are held to
+    the oracle's bound."""
     rng, _, _, payload = case("PQ2_0_G128", n, k, seed=n + 5 * k)
     xr = rand_x(rng, k, "f16")
     say("gemv g64 vs planes n=%d k=%d" % (n, k))
@@ -121,7 +125,12 @@ def test_gemv_g64_equals_plane_gemv(n, k):
     y1 = tq.gemv_g64(tq.expand_g64(pd, "PQ2_0_G128", n, k), n, k, xd)
     y2 = tq.gemv_rowsplit(pd, "PQ2_0_G128", n, k, xd)
     torch.cuda.synchronize()
-    assert torch.equal(y1, y2)
+    if k > 8192 or n * k < 2 ** 29:
+        assert torch.equal(y1, y2)
+    else:
+        expect, bound = P.project_payload("PQ2_0_G128", n, k, payload, x_f64(xr, "f16"))
+        assert_within(to_f64(torch, y1), expect, bound, "g64 n=%d k=%d" % (n, k))
+        assert_within(to_f64(torch, y2), expect, bound, "planes n=%d k=%d" % (n, k))
 
 
 def test_gemv_g64_rejects_batch_above_one():

@@ -15,7 +15,10 @@ and an all-zero row must come out exactly 0 whatever its scales.
 Every batch-1 entry point that runs this arithmetic is covered: the GEMV on
 a rotated input, the one-launch decode step (transform inside), the
 one-launch output head (RMSNorm and transform inside), and the GEMV over the
-expanded G64 block stream.
+expanded G64 block stream.  Large matrices (2^29 weights and more) take the
+matrix-core kernel, whose activation digits and block sums are a different
+arithmetic: the *_large tests repeat the 2400 hard rows 55 times (132000
+rows) and hold every output to the same bar.
 """
 
 import numpy as np
@@ -181,3 +184,92 @@ def test_gemv_g64_hard_rows(k, xkind):
     bound = P.REL * (np.abs(w[:, :k]) @ np.abs(xrot64)) + P.ABS
     assert_within(got, expect, bound, "g64 k=%d %s" % (k, xkind))
     assert np.all(got[zero_rows] == 0.0)
+
+
+# ---------------------------------------------------- large matrices -----
+REPS = 55  # 132000 rows x 5120: 6.8e8 weights
+
+
+def tile_rows(n, k, payload, reps):
+    """The payload of the n rows repeated reps times (row r of copy m is row
+    r + n*m), plane by plane."""
+    gs, gb = tq.geometry(FMT, n, k), tq.geometry(FMT, n * reps, k)
+    big = np.zeros(gb["payload_bytes"], np.uint8)
+    for plane in ("base", "high", "scale"):
+        nb = gs[plane + "_bytes"]
+        if nb:
+            src = payload[gs[plane + "_offset"]:gs[plane + "_offset"] + nb]
+            big[gb[plane + "_offset"]:gb[plane + "_offset"] + nb * reps] = np.tile(src, reps)
+    return big
+
+
+def check_tiled(got, expect, bound, zero_rows, what):
+    rows = got.reshape(REPS, N)
+    for m in (0, 1, REPS // 2, REPS - 1):
+        assert_within(rows[m], expect, bound, "%s copy %d" % (what, m))
+    worst = np.abs(rows - expect[None, :]) / bound[None, :]
+    assert float(worst.max()) <= 1.0, "%s: worst |err|/bound over all copies %r" % (what, float(worst.max()))
+    z = rows[:, zero_rows]
+    assert np.all(z == 0.0), "%s: all-zero rows must give exactly 0" % what
+
+
+@pytest.mark.parametrize("xkind", XKINDS)
+def test_gemv_rowsplit_hard_rows_large(xkind):
+    k = 5120
+    rng = np.random.default_rng(5 * k + len(xkind))
+    xrot = activation(rng, k, xkind).astype(np.float16)
+    xrot64 = xrot.astype(np.float64)
+    trits, sb, zero_rows = hard_rows(rng, N, k, xrot64)
+    payload = tq.pack_rowsplit(FMT, trits, sb)
+    say("gemv hard rows large n=%d k=%d x=%s" % (N * REPS, k, xkind))
+    y = tq.gemv_rowsplit(dev(torch, tile_rows(N, k, payload, REPS)), FMT, N * REPS, k,
+                         dev(torch, row2d(xrot)))
+    torch.cuda.synchronize()
+    expect, bound = P.project_payload(FMT, N, k, payload, xrot64[None, :])
+    check_tiled(y.cpu().numpy()[0].astype(np.float64), expect[0], bound[0], zero_rows,
+                "gemv large %s" % xkind)
+
+
+@pytest.mark.parametrize("xkind", XKINDS)
+def test_rotated_gemv_hard_rows_large(xkind):
+    k = 5120
+    rng = np.random.default_rng(6 * k + len(xkind))
+    xb = synth.f32_to_bf16_bits(row2d(activation(rng, k, xkind)))
+    sbits = synth.sign_bits(rng, k)
+    xrot64 = T.forward(x_f64(xb, "bf16"), T.bf16_bits_to_f64(sbits))
+    trits, sb, zero_rows = hard_rows(rng, N, k, xrot64[0])
+    payload = tq.pack_rowsplit(FMT, trits, sb)
+    say("rotated gemv hard rows large n=%d k=%d x=%s" % (N * REPS, k, xkind))
+    y = tq.rotated_gemv_rowsplit(dev(torch, tile_rows(N, k, payload, REPS)), FMT, N * REPS, k,
+                                 x_dev(torch, xb, "bf16"), signs_dev(torch, sbits))
+    torch.cuda.synchronize()
+    expect, bound = P.project_payload(FMT, N, k, payload, xrot64)
+    check_tiled(y.cpu().numpy()[0].astype(np.float64), expect[0], bound[0], zero_rows,
+                "rotated large %s" % xkind)
+
+
+@pytest.mark.parametrize("xkind", XKINDS)
+def test_head_hard_rows_large(xkind):
+    k = 5120
+    rng = np.random.default_rng(7 * k + len(xkind))
+    xb = synth.f32_to_bf16_bits(row2d(activation(rng, k, xkind)))
+    sbits = synth.sign_bits(rng, k)
+    gbits = synth.norm_weight_bits(rng, k)
+    eps = 1e-6
+    xrot64 = T.forward(Hd.rmsnorm(x_f64(xb, "bf16"), T.bf16_bits_to_f64(gbits), eps),
+                       T.bf16_bits_to_f64(sbits))
+    trits, sb, zero_rows = hard_rows(rng, N, k, xrot64[0])
+    payload = tq.pack_rowsplit(FMT, trits, sb)
+    say("head hard rows large n=%d k=%d x=%s" % (N * REPS, k, xkind))
+    work = torch.zeros(2, dtype=torch.int64, device="cuda")
+    logits = torch.empty(N * REPS, dtype=torch.float32, device="cuda")
+    gd = dev(torch, gbits.view(np.int16)).view(torch.bfloat16)
+    tok = tq.head_argmax(dev(torch, tile_rows(N, k, payload, REPS)), FMT, N * REPS, k,
+                         x_dev(torch, xb, "bf16"), gd, eps, signs_dev(torch, sbits), work, logits=logits)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy().astype(np.float64)
+    logits_o, bound, _ = Hd.head(FMT, N, k, payload, x_f64(xb, "bf16"), T.bf16_bits_to_f64(gbits),
+                                 eps, T.bf16_bits_to_f64(sbits))
+    check_tiled(lg, logits_o[0], bound[0], zero_rows, "head large %s" % xkind)
+    t = int(tok.item())
+    assert t == int(np.flatnonzero(lg == lg.max())[0]) and t < N
