@@ -28,21 +28,24 @@
 // (i, gA) byte r multiplies B lane group 2(r/16) + gA/2, nibble
 // r%16 + 16(gA%2); so the even group's digits sit in A lanes gA = 0, 1, the
 // odd group's in gA = 2, 3, and the other half of every A lane is zero.
-// Per 512-weight line u of a row (groups 4u..4u+3) a lane makes two 16-byte
-// loads L = 0, 1 of its row: lane group g takes bytes 64L + 32(g%2) +
-// 16(g/2), i.e. half g/2 of group 4u + 2L + g%2, and each load feeds a chain
-// of two MFMAs (m = 0, 1: code dwords 2m, 2m+1).  D lane group g then holds
-// four digits of the group its own load came from, so it folds the chain
-// with that group's scale: acc += s * sum_v (D[v] - X[v]), where X is the
-// same chain on all-ones codes (every weight 0) -- identical instructions on
-// identical operands, so an all-zero group adds exactly nothing and an
-// all-zero row is exactly 0 ([gguf-explainer] §4.4 offset form).
-//
+// Per 512-weight line u of a row (groups 4u..4u+3) lane (j, g) takes two
+// 16-byte pieces L = 0, 1 of row j: bytes 64L + 32(g%2) + 16(g/2), i.e.
+// half g/2 of group 4u + 2L + g%2, and each piece feeds a chain of two MFMAs
+// (m = 0, 1: code dwords 2m, 2m+1, as fp4 dwords even(2m), odd(2m),
+// even(2m+1), odd(2m+1) -- even/odd: the dword's codes 4b, 4b+2 or 4b+1,
+// 4b+3).  D lane group g then holds four digits of the group its own piece
+// came from, so it folds the chain with that group's scale:
+// acc += s * sum_v (D[v] - X[v]), where X is the chain's value on all-ones
+// codes (every weight 0).  Both are exact, so an all-zero group gives
+// D = X bit for bit and adds nothing, and an all-zero row is exactly 0
+// ([gguf-explainer] §4.4 offset form).
+
 // Work split.  A wave owns blocks of 16T consecutive rows (T tiles of 16);
 // per line u it reads the A operands once from LDS and runs T tiles with
-// them.  Its loads (two code loads and one 8-byte scale load per tile and
-// line) run DEP = UD*T ahead in a ring that continues into the wave's next
-// block, so the stream never drains between blocks.
+// them.  Its loads (two code loads per tile and line, one scale load per
+// round of UD lines) run one round (DEP = UD*T slots) ahead in a ring that
+// continues into the wave's next block, so the stream never drains between
+// blocks.
 
 #pragma once
 
@@ -56,9 +59,13 @@ typedef int i32x8_f4 __attribute__((ext_vector_type(8)));
 typedef float f32x4_f4 __attribute__((ext_vector_type(4)));
 
 // LDS table of A operands: per line u, blocks (L, m, c) of 32 lane slots of
-// 16 bytes (slot gA*8 + digit) and one zero slot read by the lanes whose
-// half is empty.
-constexpr int F4_BLOCK = 33 * 16;
+// 16 bytes (slot gA*8 + digit, at byte 16 + 16 slot) between two zero slots
+// read by the lanes whose half is empty.  A 16-byte LDS read serves 16
+// lanes (one lane group) per pass from 64 four-byte banks: the active lanes
+// of group gA read slots 8gA..8gA+7, banks 32(gA%2)+4..+35 of the block, so
+// the even groups' empty lanes read the zero slot at byte 0 (banks 0-3) and
+// the odd groups' the one at byte 528 (banks 4-7), away from their data.
+constexpr int F4_BLOCK = 34 * 16;
 constexpr int F4_UNIT = 8 * F4_BLOCK;
 
 __device__ __forceinline__ f32x4_f4 mfma_f4(const i32x8_f4 &a, const i32x8_f4 &b, const f32x4_f4 &c,
@@ -70,17 +77,19 @@ __device__ __forceinline__ f32x4_f4 mfma_f4(const i32x8_f4 &a, const i32x8_f4 &b
 // the two B operands of one 16-byte code load (see the layout above)
 __device__ __forceinline__ void f4_codes(const u32x4 &w, i32x8_f4 &b0, i32x8_f4 &b1) {
   const uint32_t m = 0x33333333u;
-  b0 = (i32x8_f4){(int)(w[0] & m), (int)(w[1] & m), (int)((w[0] >> 2) & m), (int)((w[1] >> 2) & m), 0, 0, 0, 0};
-  b1 = (i32x8_f4){(int)(w[2] & m), (int)(w[3] & m), (int)((w[2] >> 2) & m), (int)((w[3] >> 2) & m), 0, 0, 0, 0};
+  b0 = (i32x8_f4){(int)(w[0] & m), (int)((w[0] >> 2) & m), (int)(w[1] & m), (int)((w[1] >> 2) & m), 0, 0, 0, 0};
+  b1 = (i32x8_f4){(int)(w[2] & m), (int)((w[2] >> 2) & m), (int)(w[3] & m), (int)((w[3] >> 2) & m), 0, 0, 0, 0};
 }
 
 // LDS bytes of the kernel for rows of k weights
 // Per wave, used in the main loop only (so it shares its space with the
 // binary16 activations of the prologue): the two 64-byte halves of a slot's
-// 16 rows (rows 80 bytes apart), and the round's scale load as the lanes
-// hold it (16 bytes per lane: groups 8r..8r+7 of row l of the block).
-constexpr int F4_STAGE_ROW = 80;
-constexpr int F4_STAGE_CODES = 2 * 16 * F4_STAGE_ROW;
+// 16 rows, and the round's scale load as the lanes hold it (16 bytes per
+// lane: groups 8r..8r+7 of row l of the block).  Chunk q of row r sits at
+// 64r + 16(q ^ (r/4 % 4)): the quad writes (rows 4a..4a+3 per pass) and the
+// MFMA-layout reads (rows 0..15 of one chunk per pass) then both meet 16
+// distinct bank quadruples.
+constexpr int F4_STAGE_CODES = 2 * 16 * 64;
 constexpr int F4_STAGE = F4_STAGE_CODES + 64 * 16;
 
 inline size_t gemv_f4_lds(int64_t k, int wpg) {
@@ -88,6 +97,12 @@ inline size_t gemv_f4_lds(int64_t k, int wpg) {
   const int64_t stage = (int64_t)F4_STAGE * wpg;
   return (size_t)(nu * F4_UNIT + nu * 8 * 16 + 16 * wpg + (stage > 2 * k ? stage : 2 * k));
 }
+
+// An empty statement that reads and rewrites v: the loads that produce v
+// stay ahead of it in program order (with a conditional use only, the
+// compiler may move them into the branch, behind later loads, so that
+// waiting for them also waits for those).
+__device__ __forceinline__ void f4_keep(u32x4 &v) { asm volatile("" : "+v"(v)); }
 
 struct F4Slot {
   u32x4 c0, c1;  // code loads L = 0, 1
@@ -162,51 +177,52 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
   auto load_scales = [&](__amdgpu_buffer_rsrc_t rs, int r) {
     scr = __builtin_amdgcn_raw_buffer_load_b128(rs, sc_off, 16 * r, 0);
   };
+  // h[m]: binary16 elements 2m, 2m+1 of the thread's chunk x'[16c..16c+15]
+  // (c = thread index; k <= 16 * 64 * WPG)
+  const int c = tid;
+  const bool mine = c < (int)(p.k >> 4);
+  uint32_t h[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
   if constexpr (!FUSED) {
-    // one 16-element chunk per thread (k <= 16 * 64 * WPG)
-    const int c = tid;
-    const bool mine = c < (int)(p.k >> 4);
     Raw16<XD> xr;
     load16_raw<XD>(x, 16 * (int64_t)(mine ? c : 0), xr);
     __builtin_amdgcn_sched_barrier(0);
-  {
-    const auto rc = code_rsrc(gw), rs = scale_rsrc(gw);
+    {
+      const auto rc = code_rsrc(gw), rs = scale_rsrc(gw);
 #pragma unroll
-    for (int d = 0; d < DEP; ++d) {
-      load_slot(ring[d], rc, rs, d / T, d % T);
-      if (d == 0) load_scales(rs, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-    if (mine) {
-      uint32_t h[8];
-      if constexpr (XD == DT_F16) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) { h[m] = xr.q[0][m]; h[4 + m] = xr.q[1][m]; }
-      } else {
-        float v[16];
-        convert16<XD>(xr, v);
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-          h[m] = (uint32_t)f32_to_f16(v[2 * m]) | ((uint32_t)f32_to_f16(v[2 * m + 1]) << 16);
+      for (int d = 0; d < DEP; ++d) {
+        load_slot(ring[d], rc, rs, d / T, d % T);
+        if (d == 0) load_scales(rs, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      u32x4 *o = reinterpret_cast<u32x4 *>(xh + 16 * c);
-      o[0] = (u32x4){h[0], h[1], h[2], h[3]};
-      o[1] = (u32x4){h[4], h[5], h[6], h[7]};
     }
+#pragma unroll
+    for (int q = 0; q < (XD == DT_F32 ? 4 : 2); ++q) f4_keep(xr.q[q]);
+    if constexpr (XD == DT_F16) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) { h[m] = xr.q[0][m]; h[4 + m] = xr.q[1][m]; }
+    } else {
+      float v[16];
+      convert16<XD>(xr, v);
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        h[m] = (uint32_t)f32_to_f16(v[2 * m]) | ((uint32_t)f32_to_f16(v[2 * m + 1]) << 16);
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) h[m] = mine ? h[m] : 0u;
   } else {
     // the signed transform of one 1024-element block per wave (k <= 1024 *
-    // WPG), as the wave kernel does it, the wave's scratch in the table's space
+    // WPG), as the wave kernel does it, the wave's scratch in the table's
+    // space; x' goes through LDS to the threads that own its chunks
     const int blk1 = wave;
-    const bool mine = blk1 < NB;
-    const int64_t e = (int64_t)(mine ? blk1 : 0) * 1024 + 16 * lane;
+    const bool tw = blk1 < NB;
+    const int64_t e = (int64_t)(tw ? blk1 : 0) * 1024 + 16 * lane;
     Raw16<XD> xr;
     if constexpr (MODE == MODE_ROT)
       load16_raw<XD>(x, hd.tiles ? (int64_t)head_src((int)e, hd.tiles, hd.groups, hd.head_dim) : e, xr);
     else
       load16_raw<XD>(x, e, xr);
     const u32x4 *sp = reinterpret_cast<const u32x4 *>(signs + e);
-    const u32x4 s0 = sp[0], s1 = sp[1];
+    u32x4 s0 = sp[0], s1 = sp[1];
     u32x4 g0 = {0u, 0u, 0u, 0u}, g1 = {0u, 0u, 0u, 0u};
     if constexpr (HEAD) {
       const u32x4 *gp = reinterpret_cast<const u32x4 *>(hd.g + e);
@@ -214,31 +230,40 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
       g1 = gp[1];
     }
     __builtin_amdgcn_sched_barrier(0);
-  {
-    const auto rc = code_rsrc(gw), rs = scale_rsrc(gw);
+    {
+      const auto rc = code_rsrc(gw), rs = scale_rsrc(gw);
 #pragma unroll
-    for (int d = 0; d < DEP; ++d) {
-      load_slot(ring[d], rc, rs, d / T, d % T);
-      if (d == 0) load_scales(rs, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int d = 0; d < DEP; ++d) {
+        load_slot(ring[d], rc, rs, d / T, d % T);
+        if (d == 0) load_scales(rs, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-  }
+#pragma unroll
+    for (int q = 0; q < (XD == DT_F32 ? 4 : 2); ++q) f4_keep(xr.q[q]);
+    f4_keep(s0);
+    f4_keep(s1);
+    if constexpr (HEAD) {
+      f4_keep(g0);
+      f4_keep(g1);
+    }
     float v[16];
     float sq = 0.0f;
-    if (mine) {
-      convert16<XD>(xr, v);
-      if constexpr (HEAD) {
+    convert16<XD>(xr, v);
+    if constexpr (HEAD) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) sq = __builtin_fmaf(v[q], v[q], sq);
-        const uint32_t gw8[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+      for (int q = 0; q < 16; ++q) sq = __builtin_fmaf(v[q], v[q], sq);
+      sq = tw ? sq : 0.0f;
+      const uint32_t gw8[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
 #pragma unroll
-        for (int q = 0; q < 16; ++q) v[q] *= bf16_to_f32((uint16_t)(gw8[q >> 1] >> (16 * (q & 1))));
-      }
+      for (int q = 0; q < 16; ++q) v[q] *= bf16_to_f32((uint16_t)(gw8[q >> 1] >> (16 * (q & 1))));
+    }
+    {
       const uint32_t sw[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
 #pragma unroll
       for (int q = 0; q < 16; ++q) v[q] = apply_sign(v[q], (uint16_t)(sw[q >> 1] >> (16 * (q & 1))));
-      wht1024_wave(v, lane, reinterpret_cast<float *>(tab) + 1024 * wave);
     }
+    if (tw) wht1024_wave(v, lane, reinterpret_cast<float *>(tab) + 1024 * wave);
     float post = 0.03125f;
     if constexpr (HEAD) {
 #pragma unroll
@@ -250,7 +275,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
       for (int w = 0; w < nst; ++w) tot += red[w];
       post = 0.03125f / __builtin_sqrtf(tot / (float)(NB * 1024) + hd.eps);
     }
-    if (mine) {
+    if (tw) {
       uint16_t *o = xh + blk1 * 1024;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -260,15 +285,22 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
         *reinterpret_cast<u32x2 *>(o + 256 * q + 4 * lane) = (u32x2){lo, hi};
       }
     }
+    __syncthreads();
+    if (mine) {
+      const u32x4 *q = reinterpret_cast<const u32x4 *>(xh + 16 * c);
+      const u32x4 a0 = q[0], a1 = q[1];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) { h[m] = a0[m]; h[4 + m] = a1[m]; }
+    }
   }
-  __syncthreads();
 
   // ---- 2. U: the power of two with max|x'| < 8U over the finite elements
   {
     float mx = 0.0f;
-    for (int c = tid; c < (int)(p.k >> 1); c += 64 * WPG) {
-      const uint32_t w = reinterpret_cast<const uint32_t *>(xh)[c];
-      const float a = __builtin_fabsf(f16_to_f32((uint16_t)w)), b = __builtin_fabsf(f16_to_f32((uint16_t)(w >> 16)));
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const float a = __builtin_fabsf(f16_to_f32((uint16_t)h[m]));
+      const float b = __builtin_fabsf(f16_to_f32((uint16_t)(h[m] >> 16)));
       mx = (a <= 65504.0f && a > mx) ? a : mx;
       mx = (b <= 65504.0f && b > mx) ? b : mx;
     }
@@ -284,44 +316,65 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
   const int E = mx > 0.0f ? (int)((__float_as_uint(mx) >> 23) & 0xFF) - 126 : 0;
   const float inv_u = __builtin_ldexpf(1.0f, 3 - E);
 
-  // ---- 3. the digit table: chunk (u, L, m, c, gA) holds digit p of the 16
-  // elements 128(4u + 2L + gA/2) + 64c + 32m + 2b + gA%2, b = 0..15
-  for (int ch = tid; ch < NU * 32; ch += 64 * WPG) {
-    const int gA = ch & 3, c = (ch >> 2) & 1, m = (ch >> 3) & 1, L = (ch >> 4) & 1, u = ch >> 5;
-    const int e0 = 128 * (4 * u + 2 * L + (gA >> 1)) + 64 * c + 32 * m + (gA & 1);
+  // ---- 3. the digit table and the all-ones sums.  Thread c's 16 elements
+  // form chunk (u, L, m, half, gA) = (c/32, c/16 % 2, c/2 % 2, c/4 % 2,
+  // 2(c/8 % 2) + c % 2) of the table: byte b of a slot holds element
+  // 16c + 2(b % 8) + b/8 (the order f4_codes gives the codes).  The all-ones
+  // product of a group and digit p, 2^(E-3-4p) times the sum of that digit
+  // over the group's 128 elements, is exact both in the MFMA and here
+  // (integer digit sums), so it is the same value; the group's 8 chunks are
+  // 8 neighbouring lanes, which add their digit sums.
+  {
     float r[16];
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
-      const float v = f16_to_f32(xh[e0 + 2 * b]);
-      r[b] = __builtin_fabsf(v) <= 65504.0f ? v * inv_u : __builtin_nanf("");
+    for (int m = 0; m < 8; ++m) {
+      const float lo = f16_to_f32((uint16_t)h[m]), hi = f16_to_f32((uint16_t)(h[m] >> 16));
+      r[m] = __builtin_fabsf(lo) <= 65504.0f ? lo * inv_u : __builtin_nanf("");
+      r[8 + m] = __builtin_fabsf(hi) <= 65504.0f ? hi * inv_u : __builtin_nanf("");
     }
-    uint8_t *blk = tab + u * F4_UNIT + ((L * 2 + m) * 2 + c) * F4_BLOCK + gA * 8 * 16;
+    const int grp = c >> 3;
+    const int gA = 2 * (grp & 1) + (c & 1);
+    uint8_t *blk = tab + (c >> 5) * F4_UNIT + ((((c >> 4) & 1) * 2 + ((c >> 1) & 1)) * 2 + ((c >> 2) & 1)) * F4_BLOCK +
+                   16 + gA * 8 * 16;
+    float *xs = reinterpret_cast<float *>(xt) + 8 * grp;
+    if (mine) {
+      // one digit per pass (unrolled, the passes would hold every digit's
+      // temporaries at once and cost the main loop its occupancy)
+#pragma unroll 1
+      for (int d = 0; d < 8; ++d) {
+        uint32_t w[4];
+        float sum = 0.0f;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      uint32_t w[4];
+        for (int q = 0; q < 4; ++q) {
+          float qq[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float qq[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qq[e] = __builtin_rintf(r[4 * q + e]);
-          r[4 * q + e] = (r[4 * q + e] - qq[e]) * 16.0f;
+          for (int e = 0; e < 4; ++e) {
+            qq[e] = __builtin_rintf(r[4 * q + e]);
+            r[4 * q + e] = (r[4 * q + e] - qq[e]) * 16.0f;
+            sum += qq[e];
+          }
+          int pk = __builtin_amdgcn_cvt_pk_fp8_f32(qq[0], qq[1], 0, false);
+          pk = __builtin_amdgcn_cvt_pk_fp8_f32(qq[2], qq[3], pk, true);
+          w[q] = (uint32_t)pk;
         }
-        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(qq[0], qq[1], 0, false);
-        pk = __builtin_amdgcn_cvt_pk_fp8_f32(qq[2], qq[3], pk, true);
-        w[q] = (uint32_t)pk;
+        *reinterpret_cast<u32x4 *>(blk + d * 16) = (u32x4){w[0], w[1], w[2], w[3]};
+        // the group's 8 chunks are lanes 8a..8a+7 of this wave
+        sum += __shfl_xor(sum, 1);
+        sum += __shfl_xor(sum, 2);
+        sum += __shfl_xor(sum, 4);
+        if ((c & 7) == 0) xs[d] = sum * __builtin_ldexpf(1.0f, E - 3 - 4 * d);
       }
-      *reinterpret_cast<u32x4 *>(blk + d * 16) = (u32x4){w[0], w[1], w[2], w[3]};
     }
   }
   // zero slots
-  for (int z = tid; z < NU * 8; z += 64 * WPG)
-    *reinterpret_cast<u32x4 *>(tab + (z >> 3) * F4_UNIT + (z & 7) * F4_BLOCK + 32 * 16) = (u32x4){0u, 0u, 0u, 0u};
+  for (int z = tid; z < NU * 16; z += 64 * WPG)
+    *reinterpret_cast<u32x4 *>(tab + (z >> 4) * F4_UNIT + ((z >> 1) & 7) * F4_BLOCK + (z & 1) * 33 * 16) =
+        (u32x4){0u, 0u, 0u, 0u};
   __syncthreads();
 
-  // ---- 4. the lane's A slot, its row's digit scale, and the all-ones sums
+  // ---- 4. the lane's A slot and its row's digit scale
   const bool act = ((j >> 2) & 1) == (g >> 1);
-  const int a_off = (act ? g * 8 + (j & 3) + 4 * (j >> 3) : 32) * 16;
+  const int a_off = act ? 16 + (g * 8 + (j & 3) + 4 * (j >> 3)) * 16 : (g & 1) * 33 * 16;
   const int sa = 127 + E - 2 - 4 * ((j & 3) + 4 * (j >> 3));
   auto read_a = [&](int u, int L, int m) -> i32x8_f4 {
     const uint8_t *b = tab + u * F4_UNIT + (L * 2 + m) * 2 * F4_BLOCK + a_off;
@@ -329,17 +382,6 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
     const u32x4 hi = *reinterpret_cast<const u32x4 *>(b + F4_BLOCK);
     return (i32x8_f4){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
-  {
-    const i32x8_f4 ones = {0x11111111, 0x11111111, 0x11111111, 0x11111111, 0, 0, 0, 0};
-    const f32x4_f4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int f = wave; f < 2 * NU; f += WPG) {
-      const int u = f >> 1, L = f & 1;
-      f32x4_f4 dd = mfma_f4(read_a(u, L, 0), ones, zero, sa);
-      dd = mfma_f4(read_a(u, L, 1), ones, dd, sa);
-      if (j == 0) xt[(u * 2 + L) * 4 + g] = dd;
-    }
-  }
-  __syncthreads();
 
   // ---- 5. the blocks, as one flat sequence of rounds: round q of the wave
   // is line group r = q % NR of its block gw + (q / NR) W, and the ring's
@@ -371,15 +413,16 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
       const int u = r * UD + ud;
       const i32x8_f4 a00 = read_a(u, 0, 0), a01 = read_a(u, 0, 1);
       const i32x8_f4 a10 = read_a(u, 1, 0), a11 = read_a(u, 1, 1);
-      const f32x4_f4 x0 = xt[(u * 2) * 4 + g], x1 = xt[(u * 2 + 1) * 4 + g];
+      // the all-ones sums of the lane's group (4u + 2L + g%2) and digits
+      const f32x4_f4 x0 = xt[(4 * u + (g & 1)) * 2 + (g >> 1)], x1 = xt[(4 * u + 2 + (g & 1)) * 2 + (g >> 1)];
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         F4Slot &s = ring[ud * T + t];
         i32x8_f4 b00, b01, b10, b11;
-        st[ld_row * (F4_STAGE_ROW / 16) + ld_q] = s.c0;
-        st[(16 + ld_row) * (F4_STAGE_ROW / 16) + ld_q] = s.c1;
-        const u32x4 c0 = st[j * (F4_STAGE_ROW / 16) + rd_q];
-        const u32x4 c1 = st[(16 + j) * (F4_STAGE_ROW / 16) + rd_q];
+        st[ld_row * 4 + (ld_q ^ ((ld_row >> 2) & 3))] = s.c0;
+        st[(16 + ld_row) * 4 + (ld_q ^ ((ld_row >> 2) & 3))] = s.c1;
+        const u32x4 c0 = st[j * 4 + (rd_q ^ (j >> 2))];
+        const u32x4 c1 = st[(16 + j) * 4 + (rd_q ^ (j >> 2))];
         f4_codes(c0, b00, b01);
         f4_codes(c1, b10, b11);
         const u32x2 sv = reinterpret_cast<const u32x2 *>(sst + 16 * t + j)[ud];
