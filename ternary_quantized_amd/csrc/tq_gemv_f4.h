@@ -104,6 +104,38 @@ inline size_t gemv_f4_lds(int64_t k, int wpg) {
 // waiting for them also waits for those).
 __device__ __forceinline__ void f4_keep(u32x4 &v) { asm volatile("" : "+v"(v)); }
 
+// Lane reductions with DPP row operations and lane reads (the generic
+// shuffle goes through LDS and waits for it at every step).
+template <int CTRL>
+__device__ __forceinline__ float f4_dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// in lane 8a: the sum over lanes 8a..8a+7 (quad swaps, then the next quad)
+__device__ __forceinline__ float f4_sum8(float v) {
+  v += f4_dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += f4_dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += f4_dpp<0x104>(v);  // row_shl:4
+  return v;
+}
+__device__ __forceinline__ float f4_lane(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+// the wave's maximum / sum, in every lane
+__device__ __forceinline__ float f4_wave_max(float v) {
+  v = __builtin_fmaxf(v, f4_dpp<0xB1>(v));
+  v = __builtin_fmaxf(v, f4_dpp<0x4E>(v));
+  v = __builtin_fmaxf(v, f4_dpp<0x104>(v));
+  v = __builtin_fmaxf(v, f4_dpp<0x108>(v));  // row_shl:8
+  return __builtin_fmaxf(__builtin_fmaxf(f4_lane(v, 0), f4_lane(v, 16)), __builtin_fmaxf(f4_lane(v, 32), f4_lane(v, 48)));
+}
+__device__ __forceinline__ float f4_wave_sum(float v) {
+  v += f4_dpp<0xB1>(v);
+  v += f4_dpp<0x4E>(v);
+  v += f4_dpp<0x104>(v);
+  v += f4_dpp<0x108>(v);
+  return (f4_lane(v, 0) + f4_lane(v, 16)) + (f4_lane(v, 32) + f4_lane(v, 48));
+}
+
 struct F4Slot {
   u32x4 c0, c1;  // code loads L = 0, 1
 };
@@ -266,8 +298,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
     if (tw) wht1024_wave(v, lane, reinterpret_cast<float *>(tab) + 1024 * wave);
     float post = 0.03125f;
     if constexpr (HEAD) {
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) sq += __shfl_xor(sq, o);
+      sq = f4_wave_sum(sq);
       if (lane == 0) red[wave] = sq;
       __syncthreads();
       float tot = 0.0f;
@@ -275,16 +306,26 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
       for (int w = 0; w < nst; ++w) tot += red[w];
       post = 0.03125f / __builtin_sqrtf(tot / (float)(NB * 1024) + hd.eps);
     }
+    // x' as binary16 to LDS, and the block's largest finite |x'| (the
+    // barrier that publishes x' publishes the maxima too)
+    float mxl = 0.0f;
     if (tw) {
       uint16_t *o = xh + blk1 * 1024;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = (uint32_t)f32_to_f16(v[4 * q] * post) | ((uint32_t)f32_to_f16(v[4 * q + 1] * post) << 16);
-        const uint32_t hi =
-            (uint32_t)f32_to_f16(v[4 * q + 2] * post) | ((uint32_t)f32_to_f16(v[4 * q + 3] * post) << 16);
-        *reinterpret_cast<u32x2 *>(o + 256 * q + 4 * lane) = (u32x2){lo, hi};
+        uint16_t e4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          e4[e] = f32_to_f16(v[4 * q + e] * post);
+          const float a = __builtin_fabsf(f16_to_f32(e4[e]));
+          mxl = (a <= 65504.0f && a > mxl) ? a : mxl;
+        }
+        *reinterpret_cast<u32x2 *>(o + 256 * q + 4 * lane) =
+            (u32x2){(uint32_t)e4[0] | ((uint32_t)e4[1] << 16), (uint32_t)e4[2] | ((uint32_t)e4[3] << 16)};
       }
     }
+    mxl = f4_wave_max(mxl);
+    if (lane == 0) red[WPG + wave] = mxl;
     __syncthreads();
     if (mine) {
       const u32x4 *q = reinterpret_cast<const u32x4 *>(xh + 16 * c);
@@ -295,7 +336,8 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
   }
 
   // ---- 2. U: the power of two with max|x'| < 8U over the finite elements
-  {
+  // (the fused modes found their maxima with the transform)
+  if constexpr (!FUSED) {
     float mx = 0.0f;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -304,11 +346,10 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
       mx = (a <= 65504.0f && a > mx) ? a : mx;
       mx = (b <= 65504.0f && b > mx) ? b : mx;
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = __builtin_fmaxf(mx, __shfl_xor(mx, o));
+    mx = f4_wave_max(mx);
     if (lane == 0) red[WPG + wave] = mx;
+    __syncthreads();
   }
-  __syncthreads();
   float mx = 0.0f;
 #pragma unroll
   for (int w = 0; w < WPG; ++w) mx = __builtin_fmaxf(mx, red[WPG + w]);
@@ -359,9 +400,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
         }
         *reinterpret_cast<u32x4 *>(blk + d * 16) = (u32x4){w[0], w[1], w[2], w[3]};
         // the group's 8 chunks are lanes 8a..8a+7 of this wave
-        sum += __shfl_xor(sum, 1);
-        sum += __shfl_xor(sum, 2);
-        sum += __shfl_xor(sum, 4);
+        sum = f4_sum8(sum);
         if ((c & 7) == 0) xs[d] = sum * __builtin_ldexpf(1.0f, E - 3 - 4 * d);
       }
     }
