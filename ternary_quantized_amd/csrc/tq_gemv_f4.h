@@ -81,17 +81,19 @@ __device__ __forceinline__ void f4_codes(const u32x4 &w, i32x8_f4 &b0, i32x8_f4 
   b1 = (i32x8_f4){(int)(w[2] & m), (int)((w[2] >> 2) & m), (int)(w[3] & m), (int)((w[3] >> 2) & m), 0, 0, 0, 0};
 }
 
-// LDS bytes of the kernel for rows of k weights
 // Per wave, used in the main loop only (so it shares its space with the
-// binary16 activations of the prologue): the two 64-byte halves of a slot's
-// 16 rows, and the round's scale load as the lanes hold it (16 bytes per
-// lane: groups 8r..8r+7 of row l of the block).  Chunk q of row r sits at
-// 64r + 16(q ^ (r/4 % 4)): the quad writes (rows 4a..4a+3 per pass) and the
-// MFMA-layout reads (rows 0..15 of one chunk per pass) then both meet 16
-// distinct bank quadruples.
-constexpr int F4_STAGE_CODES = 2 * 16 * 64;
-constexpr int F4_STAGE = F4_STAGE_CODES + 64 * 16;
+// binary16 activations of the prologue):
+//  - the code tile: one 64-byte half of a slot's 16 rows, chunk q of row r
+//    at 64r + 16(q ^ (r/4 % 4)), so that the quad writes (rows 4a..4a+3 per
+//    pass) and the MFMA-layout reads (rows 0..15 of one chunk per pass)
+//    both meet 16 distinct bank quadruples;
+//  - the scale tile of the block being consumed: its rows' scale bytes as
+//    they lie in the scale plane (16T rows of k/64 bytes), at most 3 KiB.
+constexpr int F4_STAGE_CODES = 16 * 64;
+constexpr int F4_STAGE_SCALES = 3 * 1024;
+constexpr int F4_STAGE = F4_STAGE_CODES + F4_STAGE_SCALES;
 
+// LDS bytes of the kernel for rows of k weights
 inline size_t gemv_f4_lds(int64_t k, int wpg) {
   const int64_t nu = k / 512;
   const int64_t stage = (int64_t)F4_STAGE * wpg;
@@ -163,8 +165,8 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = lane & 15, g = lane >> 4;
-  u32x4 *st = reinterpret_cast<u32x4 *>(stage + F4_STAGE * wave);                   // codes
-  u32x4 *sst = reinterpret_cast<u32x4 *>(stage + F4_STAGE * wave + F4_STAGE_CODES);  // scales
+  u32x4 *st = reinterpret_cast<u32x4 *>(stage + F4_STAGE * wave);                   // code tile
+  uint8_t *sct = stage + F4_STAGE * wave + F4_STAGE_CODES;                          // scale tile
 
   // ---- the wave's rows and its load ring
   const int n32 = (int)p.n;
@@ -201,13 +203,17 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
     s.c0 = __builtin_amdgcn_raw_buffer_load_b128(rc, vo, 128 * u, 0);
     s.c1 = __builtin_amdgcn_raw_buffer_load_b128(rc, vo, 128 * u + 64, 0);
   };
-  // the scales of round r of a block: lane l < 16T reads the 16 bytes of
-  // groups 8r..8r+7 of the block's row l; the other lanes read past the
-  // buffer's end, which returns zero and fetches nothing
-  u32x4 scr;
-  const int sc_off = lane < 16 * T ? lane * gbytes : 0x7FFFFFF0;
-  auto load_scales = [&](__amdgpu_buffer_rsrc_t rs, int r) {
-    scr = __builtin_amdgcn_raw_buffer_load_b128(rs, sc_off, 16 * r, 0);
+  // A block's scale tile (16T rows of k/64 bytes, contiguous in the scale
+  // plane) in three contiguous kilobyte loads, issued with the refills of
+  // the round before the block's first and kept in registers until that
+  // round.  Every round issues the three loads so that the count of loads
+  // in flight is the same in every round; in the other rounds they point
+  // past the buffer's end, which returns zero and fetches nothing.
+  u32x4 stl[3];
+  auto load_tile = [&](__amdgpu_buffer_rsrc_t rs, bool real) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      stl[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, real ? 16 * lane + 1024 * i : 0x7FFFFFF0, 0, 0);
   };
   // h[m]: binary16 elements 2m, 2m+1 of the thread's chunk x'[16c..16c+15]
   // (c = thread index; k <= 16 * 64 * WPG)
@@ -223,7 +229,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
 #pragma unroll
       for (int d = 0; d < DEP; ++d) {
         load_slot(ring[d], rc, rs, d / T, d % T);
-        if (d == 0) load_scales(rs, 0);
+        if (d == 0) load_tile(rs, true);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -267,7 +273,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
 #pragma unroll
       for (int d = 0; d < DEP; ++d) {
         load_slot(ring[d], rc, rs, d / T, d % T);
-        if (d == 0) load_scales(rs, 0);
+        if (d == 0) load_tile(rs, true);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -444,9 +450,13 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
     tr = tr + 1 == NR ? 0 : tr + 1;
     tb = tr == 0 ? tb + W : tb;
     const auto rc = code_rsrc(tb), rs = scale_rsrc(tb);
-    // the round's scales, loaded with the previous round, through LDS to the
-    // lanes that use them
-    sst[lane] = scr;
+    // a block's first round: its scale tile, loaded with the previous
+    // round, to LDS
+    if (r == 0) {
+      u32x4 *o = reinterpret_cast<u32x4 *>(sct);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) o[64 * i + lane] = stl[i];
+    }
 #pragma unroll
     for (int ud = 0; ud < UD; ++ud) {
       const int u = r * UD + ud;
@@ -458,13 +468,14 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
       for (int t = 0; t < T; ++t) {
         F4Slot &s = ring[ud * T + t];
         i32x8_f4 b00, b01, b10, b11;
+        // the two halves through the code tile, one after the other
         st[ld_row * 4 + (ld_q ^ ((ld_row >> 2) & 3))] = s.c0;
-        st[(16 + ld_row) * 4 + (ld_q ^ ((ld_row >> 2) & 3))] = s.c1;
         const u32x4 c0 = st[j * 4 + (rd_q ^ (j >> 2))];
-        const u32x4 c1 = st[(16 + j) * 4 + (rd_q ^ (j >> 2))];
+        st[ld_row * 4 + (ld_q ^ ((ld_row >> 2) & 3))] = s.c1;
+        const u32x4 c1 = st[j * 4 + (rd_q ^ (j >> 2))];
         f4_codes(c0, b00, b01);
         f4_codes(c1, b10, b11);
-        const u32x2 sv = reinterpret_cast<const u32x2 *>(sst + 16 * t + j)[ud];
+        const u32x2 sv = *reinterpret_cast<const u32x2 *>(sct + (16 * t + j) * gbytes + 8 * u);
         const uint32_t s0 = sv[0], s1 = sv[1];
         f32x4_f4 d0 = mfma_f4(a00, b00, zero, sa);
         f32x4_f4 d1 = mfma_f4(a10, b10, zero, sa);
@@ -480,7 +491,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
         // load in flight
         __builtin_amdgcn_sched_barrier(0);
         load_slot(s, rc, rs, tr * UD + ud, t);
-        if (ud == 0 && t == 0) load_scales(rs, tr);
+        if (ud == 0 && t == 0) load_tile(rs, tr == 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }

@@ -28,7 +28,8 @@ bool gemv_f4_fits(const Planes &p) {
   // dot-product kernels finish first
   if (p.n * p.k < (int64_t(1) << 29)) return false;
   return p.fmt == FMT_PQ2 && p.k >= 1024 && p.k % 1024 == 0 && p.k % (512 * F4_UD) == 0 && p.k <= 1024 * F4_WPG && p.n >= 1 &&
-         p.n < (int64_t(1) << 30) && gemv_f4_lds(p.k, F4_WPG) <= F4_LDS_MAX;
+         p.n < (int64_t(1) << 30) && gemv_f4_lds(p.k, F4_WPG) <= F4_LDS_MAX &&
+         16 * F4_T * (p.k / 64) <= F4_STAGE_SCALES;
 }
 
 template <int XD, int MODE>
