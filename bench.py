@@ -180,12 +180,12 @@ def main():
     del g_warm, g_timed
 
     achieved = step_bytes / step_mean / 1e9
-    counters = load_counters("head_rotated_gemv_248320x5120_b1_counters.json", "tq_gemv_wave.h")
+    counters = load_counters("head_rotated_gemv_248320x5120_b1_counters.json", "tq_gemv_f4.h")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": counters["hbm_bytes_per_dispatch"] if counters else None,
-                "kernel": "gemv_wave_kernel (fused signed transform + PQ2_0 GEMV, 248320 x 5120, "
-                          "batch 1, bf16 x)",
+                "kernel": "gemv_f4_kernel (fused signed transform + PQ2_0 GEMV on the fp8 x fp4 "
+                          "matrix cores, 248320 x 5120, batch 1, bf16 x)",
                 "bytes_per_launch": step_bytes, "mean_launch_us": round(step_mean * 1e6, 3),
                 "launches": args.steps,
                 "timing": "hip events on the launch stream around the timed graph replay"}

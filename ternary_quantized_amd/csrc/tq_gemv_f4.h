@@ -535,15 +535,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
       unsigned long long m = 0;
 #pragma unroll
       for (int w = 0; w < WPG; ++w) m = wbest[w] > m ? wbest[w] : m;
-      __hip_atomic_fetch_max(&hd.work[0], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      uint32_t *done = reinterpret_cast<uint32_t *>(&hd.work[1]);
-      const uint32_t prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev == gridDim.x - 1) {
-        const unsigned long long k = __hip_atomic_load(&hd.work[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        hd.token[0] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
-        __hip_atomic_store(&hd.work[0], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      head_finish(m, hd.work, hd.token);
     }
   }
 }

@@ -110,6 +110,29 @@ __device__ __forceinline__ unsigned long long greedy_key(float v, uint32_t i) {
   return v == v ? key : 0ull;
 }
 
+// The end of a head launch, on one thread per workgroup: the workgroup's
+// largest key m goes into the launch's running maximum work[0], and the
+// workgroup that finishes last (counted in the low word of work[1]) writes
+// the token and zeroes both words.  The maximum is a returning atomic: its
+// old value comes back only once the maximum has been performed where every
+// workgroup's atomics meet, and the count is taken only after that value
+// has arrived, so the last workgroup finds every other key in place.  No
+// release or acquire ordering is needed for that; an agent-scope release
+// would also write back this compute unit's dirty L2 lines (the logits) at
+// every workgroup, which serialises the launch's end.
+__device__ __forceinline__ void head_finish(unsigned long long m, unsigned long long *work, int32_t *token) {
+  const unsigned long long old = __hip_atomic_fetch_max(&work[0], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("" ::"v"(old) : "memory");  // the maximum has returned before the count
+  uint32_t *done = reinterpret_cast<uint32_t *>(&work[1]);
+  const uint32_t prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (prev == gridDim.x - 1) {
+    const unsigned long long k = __hip_atomic_load(&work[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    token[0] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+    __hip_atomic_store(&work[0], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Batch-1 GEMV, one wave per row.
 //
@@ -607,15 +630,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
       unsigned long long m = 0;
 #pragma unroll
       for (int w = 0; w < WPG; ++w) m = wbest[w] > m ? wbest[w] : m;
-      __hip_atomic_fetch_max(&hd.work[0], m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      uint32_t *done = reinterpret_cast<uint32_t *>(&hd.work[1]);
-      const uint32_t prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev == gridDim.x - 1) {
-        const unsigned long long k = __hip_atomic_load(&hd.work[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        hd.token[0] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
-        __hip_atomic_store(&hd.work[0], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      head_finish(m, hd.work, hd.token);
     }
   }
 }
