@@ -10,7 +10,8 @@
 // is -1, 0 or +1 -- so folding the group scale into the decoded weight loses
 // nothing, and the only rounding before the fp32 accumulation is that of X
 // to binary16.  Output tiles are dealt XCD-aware: the workgroups of one XCD
-// walk one M band, so that band's X stays in that XCD's L2.
+// hold a block of tiles two M bands tall, so that its X rows and weight
+// columns are shared in that XCD's L2.
 
 #include "tq_device.h"
 #include "tq_launch.h"
@@ -152,8 +153,13 @@ __device__ __forceinline__ void gemm_planes_tile(const Planes &p, const uint16_t
 
   // X loads: row xr, halves [HX*xq, HX*xq + HX) of a step
   const int xr = t / TPR, xq = t % TPR;
-  const bool xrow_ok = m0 + xr < M;
-  const uint16_t *xsrc = X + (xrow_ok ? (m0 + xr) : 0) * ldx + HX * xq;
+  // a buffer over the tile's rows of X: rows past M read as zero, so no
+  // select zeroes them (the compiler would place such a select right after
+  // the load and wait for it there)
+  const int64_t xrows = M - m0 < TM ? M - m0 : TM;
+  const __amdgpu_buffer_rsrc_t xbuf = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(X + m0 * ldx), 0, (int)(xrows * ldx * 2), 0x00020000);
+  const int xoff = (int)((xr * ldx + HX * xq) * 2);
   // code loads (threads below 2*TN): row wr, codes [32*wh, 32*wh + 32) of a
   // step (8 bytes) and that row's group scale
   // (every thread loads codes when the tile is 256 wide: no branch, so the
@@ -164,43 +170,47 @@ __device__ __forceinline__ void gemm_planes_tile(const Planes &p, const uint16_t
   // is the wave's (its code word must be uniform in a wave)
   const int wr = !wthread ? 0 : FMT == FMT_PQ2 ? t >> 1 : (((t >> 7) << 6) | (t & 63));
   const int wh = FMT == FMT_PQ2 ? (t & 1) : __builtin_amdgcn_readfirstlane((t >> 6) & 1);
-  const bool wrow_ok = wthread && n0 + wr < p.n;
-  const int64_t wrow = wrow_ok ? n0 + wr : 0;
-  const uint8_t *wsrc = p.base + wrow * p.base_row + (FMT == FMT_PQ2 ? 8 * wh : 0);
-  const uint16_t *hsrc = reinterpret_cast<const uint16_t *>(p.high + wrow * p.high_row);
-  const uint16_t *ssrc = p.scale + wrow * p.groups;
+  // buffers over the tile's weight rows: rows past n read as zero codes and
+  // zero scales, so their decoded weights are 0 without a select
+  const int wrows = __builtin_amdgcn_readfirstlane((int)(p.n - n0 < TN ? p.n - n0 : TN));
+  const __amdgpu_buffer_rsrc_t wbuf = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(p.base + n0 * p.base_row), 0, wrows * (int)p.base_row, 0x00020000);
+  const __amdgpu_buffer_rsrc_t hbuf = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t *>(p.high + n0 * p.high_row), 0, wrows * (int)p.high_row, 0x00020000);
+  const __amdgpu_buffer_rsrc_t sbuf = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(p.scale + n0 * p.groups), 0, wrows * (int)p.groups * 2, 0x00020000);
+  const int woff = wr * (int)p.base_row + (FMT == FMT_PQ2 ? 8 * wh : 0);
+  const int hoff = wr * (int)p.high_row, soff = wr * (int)p.groups * 2;
 
   constexpr int WW = FMT == FMT_PQ2 ? 2 : 3;  // code (PQ2_0) or base (PTQ1_0) dwords per step
   uint32_t xreg[2][HX / 2], wreg[4][WW], hreg[4], sreg[4];
   auto clamp = [&](int st) { return st < nsteps ? st : nsteps - 1; };  // past the end: a harmless re-read
   auto load_x = [&](int set, int st) {
-    const int64_t k0 = (int64_t)clamp(st) * G2K;
-    const u32x4_t *q = reinterpret_cast<const u32x4_t *>(xsrc + k0);
+    const int kb = clamp(st) * G2K * 2;
 #pragma unroll
     for (int i = 0; i < XQ; ++i) {
-      const u32x4_t v = q[i];
+      const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xbuf, xoff + 16 * i, kb, 0);
 #pragma unroll
       for (int c = 0; c < 4; ++c) xreg[set][4 * i + c] = v[c];
     }
   };
   auto load_w = [&](int set, int st) {
     if (wthread) {
-      const int64_t k0 = (int64_t)clamp(st) * G2K;
+      const int g = clamp(st) * G2K / 128;  // the step's group
       if constexpr (FMT == FMT_PQ2) {
-        const u32x2_t w = *reinterpret_cast<const u32x2_t *>(wsrc + k0 / 4);
+        const u32x2_t w = __builtin_amdgcn_raw_buffer_load_b64(wbuf, woff, clamp(st) * G2K / 4, 0);
         wreg[set][0] = w[0];
         wreg[set][1] = w[1];
       } else {
-        // group k0/128, window at byte 0, 4 or 12 of its 24 base bytes
+        // group g, window at byte 0, 4 or 12 of its 24 base bytes
         const int word = 2 * (clamp(st) & 1) + wh;
         const int off = word == 0 ? 0 : word == 1 ? 4 : 12;
-        const uint32_t *w = reinterpret_cast<const uint32_t *>(wsrc + (k0 / 128) * 24 + off);
-        wreg[set][0] = w[0];
-        wreg[set][1] = w[1];
-        wreg[set][2] = w[2];
-        hreg[set] = hsrc[k0 / 128];
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+          wreg[set][i] = __builtin_amdgcn_raw_buffer_load_b32(wbuf, woff + 4 * i, g * 24 + off, 0);
+        hreg[set] = __builtin_amdgcn_raw_buffer_load_b16(hbuf, hoff, 2 * g, 0);
       }
-      sreg[set] = ssrc[k0 / 128];
+      sreg[set] = __builtin_amdgcn_raw_buffer_load_b16(sbuf, soff, 2 * g, 0);
     }
   };
   uint32_t magic = 0x64006400u;
@@ -218,8 +228,8 @@ __device__ __forceinline__ void gemm_planes_tile(const Planes &p, const uint16_t
       uint32_t lo[2], hi[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        lo[c] = xrow_ok ? x_pair_f16<XD>(xv[c]) : 0u;
-        hi[c] = xrow_ok ? x_pair_f16<XD>(xv[4 + c]) : 0u;
+        lo[c] = x_pair_f16<XD>(xv[c]);
+        hi[c] = x_pair_f16<XD>(xv[4 + c]);
       }
       u32x4_t xo;
       xo[0] = __builtin_amdgcn_perm(hi[0], lo[0], 0x05040100u);
@@ -231,7 +241,7 @@ __device__ __forceinline__ void gemm_planes_tile(const Planes &p, const uint16_t
     if (wthread) {
       const _Float16 sh = __builtin_bit_cast(_Float16, (uint16_t)sreg[wset]);
       half2_t s2;
-      s2.x = s2.y = wrow_ok ? sh : (_Float16)0.0f;
+      s2.x = s2.y = sh;
       uint32_t o[4];
       uint32_t d;
       if constexpr (FMT == FMT_PQ2) {
@@ -306,13 +316,20 @@ __device__ __forceinline__ void gemm_planes_tile(const Planes &p, const uint16_t
 #pragma unroll
   for (int q = 0; q < 4; ++q) store_piece(0, 0, 0, q, 0);
   __syncthreads();
-  for (int s = 0; s < nsteps; s += 4) {  // nsteps is even
+  // whole groups of four steps, then the two left over when nsteps % 4 ==
+  // 2 (nsteps is even): the loop's back edge then always leaves the same
+  // loads in flight, so the count the compiler waits for at its head is
+  // exact rather than zero
+  int s = 0;
+  for (; s + 4 <= nsteps; s += 4) {
     step(s, 0);
     step(s + 1, 1);
-    if (s + 2 < nsteps) {
-      step(s + 2, 2);
-      step(s + 3, 3);
-    }
+    step(s + 2, 2);
+    step(s + 3, 3);
+  }
+  if (s < nsteps) {
+    step(s, 0);
+    step(s + 1, 1);
   }
 
   // epilogue: D[i][j] of a 32x32 block is in lane j + 32*((i/4) % 2),
@@ -338,11 +355,17 @@ __device__ __forceinline__ void gemm_planes_tile(const Planes &p, const uint16_t
 
 // Work split of one launch over 256 x 256 tiles: workgroups [0, nbig) take
 // whole tiles, the rest take 128 x 64 sub-tiles (8 per tile) of the tiles
-// left over.  With `xcd` set, tiles are numbered band-major and XCD x (the
-// workgroups b with b % 8 == x) owns the contiguous tiles [x*per,
-// (x+1)*per), the first big_per of them whole; otherwise tiles go in plain
-// order.
+// left over.  Tiles are numbered in groups of GEMM_GM 256-row bands: within
+// a group the number runs down the bands first, then along N, so that
+// consecutive tiles share their activation rows in pairs and their weight
+// columns in runs.  With `xcd` set, XCD x (the workgroups b with b % 8 ==
+// x) owns the contiguous tiles [x*per, (x+1)*per), the first big_per of
+// them whole; otherwise tiles go in plain order.  The tiles one XCD holds
+// at a time then span two bands and half as many weight columns as a
+// single band would, which is fewer bytes through its L2 per round.
+constexpr int GEMM_GM = 2;
 struct GemmSplit {
+  int tiles_m;  // 256-row bands along M
   int tiles_n;  // 256-wide tiles along N
   int per;      // tiles per XCD
   int big_per;  // whole tiles per XCD
@@ -386,7 +409,12 @@ __global__ __launch_bounds__(512) void gemm_planes_kernel(Planes p, const uint16
       sub = r % 8;
     }
   }
-  const int64_t m0 = (int64_t)(tile / sp.tiles_n) * 256, n0 = (int64_t)(tile % sp.tiles_n) * 256;
+  // tile number -> (band, column tile): groups of GEMM_GM bands (the last
+  // group may hold fewer), band-minor inside a group
+  const int gsz = GEMM_GM * sp.tiles_n;
+  const int grp = tile / gsz, rest = tile - grp * gsz;
+  const int gm = sp.tiles_m - grp * GEMM_GM < GEMM_GM ? sp.tiles_m - grp * GEMM_GM : GEMM_GM;
+  const int64_t m0 = (int64_t)(grp * GEMM_GM + rest % gm) * 256, n0 = (int64_t)(rest / gm) * 256;
   if (sub < 0)
     gemm_planes_tile<FMT, XD, YD, 256, 256, 4, 2, 2>(p, X, M, ldx, Y, ldy, m0, n0, lds2, lut);
   else
@@ -399,7 +427,8 @@ static hipError_t gemm_planes_go(const Planes &p, const uint16_t *x, int64_t m, 
                               int64_t ldy, hipStream_t st) {
   GemmSplit sp;
   sp.tiles_n = (int)((p.n + 255) / 256);
-  const int total = sp.tiles_n * (int)((m + 255) / 256);
+  sp.tiles_m = (int)((m + 255) / 256);
+  const int total = sp.tiles_n * sp.tiles_m;
   const int cus = device_cus();
   // a last round that would occupy at most 1/8 of the CUs is split 8 ways
   const int left = total % cus;
