@@ -365,7 +365,9 @@ tq_status tq_rotated_gemv_rowsplit_grouped(const uint8_t *payload, uint64_t payl
  * is -1, 0 or +1); X is used as binary16 (bf16 input is rounded to binary16,
  * finite |X| <= 65504); products accumulate in fp32.  Y: y_dtype TQ_F32 or
  * TQ_BF16, [M][ldy].  M == 0 is a no-op.
- * Requirements: k % 128 == 0 (TQ_ERR_SHAPE); alignment as above. */
+ * Requirements: k % 128 == 0 and k <= 2^20 (TQ_ERR_SHAPE); ldx < 2^22
+ * (TQ_ERR_ARG: a tile of 256 rows of X is addressed with 32-bit byte
+ * offsets); alignment as above. */
 tq_status tq_gemm_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
                            int32_t format, int64_t n, int64_t k, const void *x,
                            int32_t x_dtype, int64_t m, int64_t ldx, void *y,

@@ -423,6 +423,8 @@ tq_status tq_gemm_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
   if (st != TQ_OK) return st;
   if (k % 128)
     return fail(TQ_ERR_SHAPE, "k=%lld: device projections need k %% 128 == 0", (long long)k);
+  if (k > (int64_t(1) << 20))
+    return fail(TQ_ERR_SHAPE, "k=%lld exceeds the GEMM's limit of 2^20", (long long)k);
   if (m < 0) return fail(TQ_ERR_SHAPE, "m must be >= 0");
   if (x_dtype != TQ_F16 && x_dtype != TQ_BF16)
     return fail(TQ_ERR_ARG, "x_dtype must be TQ_F16 or TQ_BF16");
@@ -431,6 +433,8 @@ tq_status tq_gemm_rowsplit(const uint8_t *payload, uint64_t payload_bytes,
   if (m == 0) return TQ_OK;
   if (!x || !y) return fail(TQ_ERR_ARG, "x and y must be non-NULL");
   if (ldx < k || ldy < n) return fail(TQ_ERR_ARG, "ldx must be >= k and ldy >= n");
+  // 256 rows of X are addressed with 32-bit byte offsets
+  if (ldx >= (int64_t(1) << 22)) return fail(TQ_ERR_ARG, "ldx must be < 2^22");
   if (!aligned(x, 16) || ldx % 8)
     return fail(TQ_ERR_ALIGN, "x must be 16-byte aligned with ldx a multiple of 8");
   if (!aligned(y, 4)) return fail(TQ_ERR_ALIGN, "y must be 4-byte aligned");

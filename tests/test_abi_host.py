@@ -144,6 +144,11 @@ def test_device_entry_validation_without_gpu():
     assert L.tq_gemm_rowsplit(DEV, pb, 142, 64, 1024, DEV, 0, 4, 1024, DEV, 0, 64, None) == 1
     assert L.tq_gemm_rowsplit(DEV, pb, 142, 64, 1024, DEV, 2, 4, 1024, DEV, 2, 64, None) == 1
     assert L.tq_gemm_rowsplit(DEV, pb, 143, 64, 1024, DEV, 2, 4, 1024, DEV, 0, 64, None) == 3
+    # GEMM limits: k <= 2^20 (shape), ldx < 2^22 (argument)
+    kb = (1 << 20) + 128
+    pbk = tq.geometry("PQ2_0_G128", 64, kb)["payload_bytes"]
+    assert L.tq_gemm_rowsplit(DEV, pbk, 142, 64, kb, DEV, 2, 4, kb, DEV, 0, 64, None) == 5
+    assert L.tq_gemm_rowsplit(DEV, pb, 142, 64, 1024, DEV, 2, 4, 1 << 22, DEV, 0, 64, None) == 1
     # fused transform + GEMV: k multiple of 1024, null signs, then the
     # requests the one-launch kernel does not cover (PTQ1_0, batch > 1)
     f = L.tq_rotated_gemv_rowsplit
