@@ -36,11 +36,13 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 // turns it into code - 1, and the product with the group scale is exactly 0
 // or +-s.
 //
-// Register ring: while step s is multiplied, register set (s+1)&1 holds
-// step s+1 (decoded and stored into the other stage between step s's MFMA
-// slices) and set s&1 is refilled with step s+2, so each global load has a
-// whole step to land.  The code loads are plain (cached) loads: one 128-byte
-// line of a weight row serves 8 consecutive steps.
+// Register ring: while step s is multiplied, X register set (s+1)&1 holds
+// step s+1, which is stored into the other stage between step s's MFMA
+// slices; each half of the set is refilled with step s+3 as soon as its two
+// pieces are stored, so every X load has two steps to land (X misses the
+// L2 often enough that one step is not enough).  The codes are fetched four
+// steps ahead; they are plain (cached) loads: one 128-byte line of a weight
+// row serves 8 consecutive steps.
 //
 // Two tile shapes share the kernel: 256 x 256 tiles (waves 2 x 4 of 128 x
 // 64) for the bulk, and 128 x 64 sub-tiles (waves 4 x 2 of 32 x 32) for the
@@ -185,14 +187,20 @@ __device__ __forceinline__ void gemm_planes_tile(const Planes &p, const uint16_t
   constexpr int WW = FMT == FMT_PQ2 ? 2 : 3;  // code (PQ2_0) or base (PTQ1_0) dwords per step
   uint32_t xreg[2][HX / 2], wreg[4][WW], hreg[4], sreg[4];
   auto clamp = [&](int st) { return st < nsteps ? st : nsteps - 1; };  // past the end: a harmless re-read
-  auto load_x = [&](int set, int st) {
+  // loads 2h and 2h+1 of step st's X share into set `set` (the two that
+  // store pieces 2h and 2h+1 read)
+  auto load_x_half = [&](int set, int st, int h) {
     const int kb = clamp(st) * G2K * 2;
 #pragma unroll
-    for (int i = 0; i < XQ; ++i) {
+    for (int i = 2 * h; i < 2 * h + 2 && i < XQ; ++i) {
       const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xbuf, xoff + 16 * i, kb, 0);
 #pragma unroll
       for (int c = 0; c < 4; ++c) xreg[set][4 * i + c] = v[c];
     }
+  };
+  auto load_x = [&](int set, int st) {
+    load_x_half(set, st, 0);
+    load_x_half(set, st, 1);
   };
   auto load_w = [&](int set, int st) {
     if (wthread) {
@@ -271,13 +279,11 @@ __device__ __forceinline__ void gemm_planes_tile(const Planes &p, const uint16_t
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  // step s: X set s&1 is refilled with step s+2 and code set s&3 with step
-  // s+4 (both already stored), stage s&1 is multiplied, and between its four
-  // 16-deep k slices step s+1 (X set (s+1)&1, code set (s+1)&3) is stored
-  // into the other stage.  Codes come from HBM, so they are fetched further
-  // ahead; X mostly hits in L2.
+  // step s: code set s&3 (already stored) is refilled with step s+4, stage
+  // s&1 is multiplied, and between its four 16-deep k slices step s+1 (X
+  // set (s+1)&1, code set (s+1)&3) is stored into the other stage, each X
+  // half refilled with step s+3 right after its last piece.
   auto step = [&](int s, int ph) {  // ph = s & 3
-    load_x(ph & 1, s + 2);
     load_w(ph, s + 4);
     const int buf = ph & 1;
     const _Float16 *As = lds2 + buf * STAGE;
@@ -304,6 +310,9 @@ __device__ __forceinline__ void gemm_planes_tile(const Planes &p, const uint16_t
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks & 1][i], bf[ks & 1][j], acc[i][j],
                                                              0, 0, 0);
       store_piece((ph + 1) & 1, (ph + 1) & 3, buf ^ 1, ks, (ph + 1) & 1);
+      // pieces ks-1 and ks have left the X registers they share: refill
+      // them at once with step s+3, which they hold next
+      if (ks & 1) load_x_half((ph + 1) & 1, s + 3, ks >> 1);
     }
     __syncthreads();
   };
@@ -314,7 +323,10 @@ __device__ __forceinline__ void gemm_planes_tile(const Planes &p, const uint16_t
 #pragma unroll
   for (int i = 1; i < 4; ++i) load_w(i, i);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) store_piece(0, 0, 0, q, 0);
+  for (int q = 0; q < 4; ++q) {
+    store_piece(0, 0, 0, q, 0);
+    if (q & 1) load_x_half(0, 2, q >> 1);
+  }
   __syncthreads();
   // whole groups of four steps, then the two left over when nsteps % 4 ==
   // 2 (nsteps is even): the loop's back edge then always leaves the same
