@@ -36,9 +36,10 @@
 // 4b+3).  D lane group g then holds four digits of the group its own piece
 // came from, so it folds the chain with that group's scale:
 // acc += s * sum_v (D[v] - X[v]), where X is the chain's value on all-ones
-// codes (every weight 0).  Both are exact, so an all-zero group gives
-// D = X bit for bit and adds nothing, and an all-zero row is exactly 0
-// ([gguf-explainer] §4.4 offset form).
+// codes (every weight 0), computed once per launch by the same MFMAs on the
+// same A operands, so an all-zero group gives D = X bit for bit and adds
+// nothing, and an all-zero row is exactly 0 ([gguf-explainer] §4.4 offset
+// form).
 
 // Work split.  A wave owns blocks of 16T consecutive rows (T tiles of 16);
 // per line u it reads the A operands once from LDS and runs T tiles with
@@ -111,13 +112,6 @@ __device__ __forceinline__ void f4_keep(u32x4 &v) { asm volatile("" : "+v"(v)); 
 template <int CTRL>
 __device__ __forceinline__ float f4_dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-// in lane 8a: the sum over lanes 8a..8a+7 (quad swaps, then the next quad)
-__device__ __forceinline__ float f4_sum8(float v) {
-  v += f4_dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += f4_dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += f4_dpp<0x104>(v);  // row_shl:4
-  return v;
 }
 __device__ __forceinline__ float f4_lane(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
@@ -363,14 +357,10 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
   const int E = mx > 0.0f ? (int)((__float_as_uint(mx) >> 23) & 0xFF) - 126 : 0;
   const float inv_u = __builtin_ldexpf(1.0f, 3 - E);
 
-  // ---- 3. the digit table and the all-ones sums.  Thread c's 16 elements
-  // form chunk (u, L, m, half, gA) = (c/32, c/16 % 2, c/2 % 2, c/4 % 2,
-  // 2(c/8 % 2) + c % 2) of the table: byte b of a slot holds element
-  // 16c + 2(b % 8) + b/8 (the order f4_codes gives the codes).  The all-ones
-  // product of a group and digit p, 2^(E-3-4p) times the sum of that digit
-  // over the group's 128 elements, is exact both in the MFMA and here
-  // (integer digit sums), so it is the same value; the group's 8 chunks are
-  // 8 neighbouring lanes, which add their digit sums.
+  // ---- 3. the digit table.  Thread c's 16 elements form chunk (u, L, m,
+  // half, gA) = (c/32, c/16 % 2, c/2 % 2, c/4 % 2, 2(c/8 % 2) + c % 2) of
+  // the table: byte b of a slot holds element 16c + 2(b % 8) + b/8 (the
+  // order f4_codes gives the codes).
   {
     float r[16];
 #pragma unroll
@@ -383,14 +373,12 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
     const int gA = 2 * (grp & 1) + (c & 1);
     uint8_t *blk = tab + (c >> 5) * F4_UNIT + ((((c >> 4) & 1) * 2 + ((c >> 1) & 1)) * 2 + ((c >> 2) & 1)) * F4_BLOCK +
                    16 + gA * 8 * 16;
-    float *xs = reinterpret_cast<float *>(xt) + 8 * grp;
     if (mine) {
       // one digit per pass (unrolled, the passes would hold every digit's
       // temporaries at once and cost the main loop its occupancy)
 #pragma unroll 1
       for (int d = 0; d < 8; ++d) {
         uint32_t w[4];
-        float sum = 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float qq[4];
@@ -398,16 +386,12 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
           for (int e = 0; e < 4; ++e) {
             qq[e] = __builtin_rintf(r[4 * q + e]);
             r[4 * q + e] = (r[4 * q + e] - qq[e]) * 16.0f;
-            sum += qq[e];
           }
           int pk = __builtin_amdgcn_cvt_pk_fp8_f32(qq[0], qq[1], 0, false);
           pk = __builtin_amdgcn_cvt_pk_fp8_f32(qq[2], qq[3], pk, true);
           w[q] = (uint32_t)pk;
         }
         *reinterpret_cast<u32x4 *>(blk + d * 16) = (u32x4){w[0], w[1], w[2], w[3]};
-        // the group's 8 chunks are lanes 8a..8a+7 of this wave
-        sum = f4_sum8(sum);
-        if ((c & 7) == 0) xs[d] = sum * __builtin_ldexpf(1.0f, E - 3 - 4 * d);
       }
     }
   }
@@ -427,6 +411,22 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
     const u32x4 hi = *reinterpret_cast<const u32x4 *>(b + F4_BLOCK);
     return (i32x8_f4){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
+
+  // ---- the all-ones sums X: per line u and piece L, the chain of its two
+  // MFMAs on all-ones codes (every weight 0).  It is the main loop's chain on
+  // the main loop's operands, so a group of zero weights gives D = X bit for
+  // bit; lane (0, g) keeps digits 4(g/2)..+3 of group 4u + 2L + g%2.
+  {
+    const i32x8_f4 ones = {0x11111111, 0x11111111, 0x11111111, 0x11111111, 0, 0, 0, 0};
+    const f32x4_f4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int pr = wave; pr < 2 * NU; pr += WPG) {
+      const int u = pr >> 1, L = pr & 1;
+      f32x4_f4 d = mfma_f4(read_a(u, L, 0), ones, z4, sa);
+      d = mfma_f4(read_a(u, L, 1), ones, d, sa);
+      if (j == 0) xt[(4 * u + 2 * L + (g & 1)) * 2 + (g >> 1)] = d;
+    }
+  }
+  __syncthreads();
 
   // ---- 5. the blocks, as one flat sequence of rounds: round q of the wave
   // is line group r = q % NR of its block gw + (q / NR) W, and the ring's
