@@ -224,7 +224,3 @@ def blocks_to_planes(fmt, n, k, blocks):
         payload[h0:h0 + geo["high_bytes"]] = blocks[:, :, h_lo:h_hi].reshape(-1)
     payload[s0:s0 + geo["scale_bytes"]] = blocks[:, :, s_lo:s_hi].reshape(-1)
     return payload
-
-
-def format_names():
-    return tuple(FORMATS)

@@ -39,11 +39,6 @@ __device__ __forceinline__ half2_t pack_h2(float a, float b) {
   return r;
 }
 
-template <int XD>
-__device__ __forceinline__ float xload(const void *x, int64_t i) {
-  return load_elem<XD>(x, i);
-}
-
 // Raw activation words of one lane chunk, as loaded (no conversion yet).
 template <int FMT, int CW, int XD>
 struct XRaw {
@@ -165,30 +160,6 @@ __device__ __forceinline__ ChunkPtr<FMT, CW> chunk_ptr(const Planes &p, int64_t 
     r.scale = p.scale + g;
   }
   return r;
-}
-
-// Raw plane bytes of one lane chunk of row `row` (always a valid row).
-template <int FMT, int CW>
-__device__ __forceinline__ void load_raw(const Planes &p, const ChunkPtr<FMT, CW> &cp, int64_t row,
-                                         Raw<FMT, CW> &r) {
-  const uint8_t *b = cp.base + row * p.base_row;
-  if constexpr (FMT == FMT_PQ2) {
-    if constexpr (CW == 64) {
-      u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(b));
-      r.w[0] = t[0]; r.w[1] = t[1]; r.w[2] = t[2]; r.w[3] = t[3];
-    } else if constexpr (CW == 32) {
-      u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(b));
-      r.w[0] = t[0]; r.w[1] = t[1];
-    } else {
-      r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(b));
-    }
-    r.h = 0;
-  } else {
-    r.w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(b));
-    r.w[1] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(b + 4));
-    r.h = cp.high[row * p.high_row];
-  }
-  r.s = cp.scale[row * p.groups];
 }
 
 // Loader cursor: the plane pointers of one lane chunk at row `row`,
@@ -326,20 +297,6 @@ __device__ __forceinline__ float seg_sum(float v) {
   if constexpr (SEG == 16)
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
                                                               0x118, 0xF, 0xF, true));
-  return v;
-}
-
-// Sum over the 16 lanes of each DPP row; the total lands in lane 15 of the
-// row (inclusive scan with row_shr 1, 2, 4, 8).
-__device__ __forceinline__ float row16_sum(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                            0x111, 0xF, 0xF, true));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                            0x112, 0xF, 0xF, true));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                            0x114, 0xF, 0xF, true));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                            0x118, 0xF, 0xF, true));
   return v;
 }
 

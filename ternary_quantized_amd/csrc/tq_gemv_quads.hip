@@ -49,10 +49,6 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ half2_t h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 __device__ __forceinline__ uint32_t u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
 
-__device__ __forceinline__ half4_t h4(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(half4_t, (u32x2){a, b});
-}
-
 // One lane's view of a chunk as loaded: the 8-byte window holding its six
 // base bytes, its group's high byte and scale bits.
 struct ChunkRaw {
@@ -75,12 +71,6 @@ __device__ __forceinline__ float blocks_sum4(const float (&v)[4]) {
   x += flt(__builtin_amdgcn_update_dpp(0u, bits(x), 0x124, 0xF, 0xF, false));  // row_ror:4
   x += flt(__builtin_amdgcn_update_dpp(0u, bits(x), 0x128, 0xF, 0xF, false));  // row_ror:8
   return x;
-}
-
-template <int XD>
-__device__ __forceinline__ float x_elem_bits(uint16_t b) {
-  if constexpr (XD == DT_BF16) return bf16_to_f32(b);
-  else return f16_to_f32(b);
 }
 
 constexpr int RQMAX = 30;  // row-quads per workgroup
