@@ -45,13 +45,21 @@ static hipError_t f4_go(const Planes &p, const void *x, const uint16_t *signs, f
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * F4_WPG, lds) != hipSuccess || per_cu < 1)
     return hipErrorInvalidConfiguration;
-  // blocks of 16T rows; the fewest passes over the resident waves, then the
-  // fewest waves with that many passes, so that every wave has the same share
+  // blocks of 16T rows.  Either the fewest passes over the resident waves,
+  // then the fewest waves with that many passes (every wave the same share),
+  // or every resident workgroup (some waves one block fewer), whichever
+  // leaves fewer compute units with one workgroup: such a unit streams its
+  // share at about half the rate.  The first is kept while it fills at
+  // least 90% of the slots.
   const int64_t nblk = (p.n + 16 * F4_T - 1) / (16 * F4_T);
-  const int64_t slots = (int64_t)device_cus() * per_cu * F4_WPG;
+  const int64_t wgs = (int64_t)device_cus() * per_cu;
+  const int64_t slots = wgs * F4_WPG;
   const int64_t passes = (nblk + slots - 1) / slots;
   const int64_t waves = (nblk + passes - 1) / passes;
-  const int64_t grid = (waves + F4_WPG - 1) / F4_WPG;
+  const int64_t even = (waves + F4_WPG - 1) / F4_WPG;
+  const int64_t need = (nblk + F4_WPG - 1) / F4_WPG;
+  const int64_t full = need < wgs ? need : wgs;
+  const int64_t grid = 10 * even >= 9 * full ? even : full;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * F4_WPG), lds, st, p, x, signs, y, hd);
   return hipGetLastError();
 }
