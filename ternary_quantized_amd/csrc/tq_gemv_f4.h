@@ -37,9 +37,10 @@
 // came from, so it folds the chain with that group's scale:
 // acc += s * sum_v (D[v] - X[v]), where X is the chain's value on all-ones
 // codes (every weight 0), computed once per launch by the same MFMAs on the
-// same A operands, so an all-zero group gives D = X bit for bit and adds
-// nothing, and an all-zero row is exactly 0 ([gguf-explainer] §4.4 offset
-// form).
+// same A operands ([gguf-explainer] §4.4 offset form).  The chain starts
+// from -X instead of 0: every sum the instruction forms is exact, so it ends
+// at D - X exactly, an all-zero group adds exactly 0 and an all-zero row is
+// exactly 0.
 
 // Work split.  A wave owns blocks of 16T consecutive rows (T tiles of 16);
 // per line u it reads the A operands once from LDS and runs T tiles with
@@ -414,8 +415,8 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
 
   // ---- the all-ones sums X: per line u and piece L, the chain of its two
   // MFMAs on all-ones codes (every weight 0).  It is the main loop's chain on
-  // the main loop's operands, so a group of zero weights gives D = X bit for
-  // bit; lane (0, g) keeps digits 4(g/2)..+3 of group 4u + 2L + g%2.
+  // the main loop's operands, kept negated as the main loop's starting
+  // value; lane (0, g) keeps digits 4(g/2)..+3 of group 4u + 2L + g%2.
   {
     const i32x8_f4 ones = {0x11111111, 0x11111111, 0x11111111, 0x11111111, 0, 0, 0, 0};
     const f32x4_f4 z4 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -423,7 +424,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
       const int u = pr >> 1, L = pr & 1;
       f32x4_f4 d = mfma_f4(read_a(u, L, 0), ones, z4, sa);
       d = mfma_f4(read_a(u, L, 1), ones, d, sa);
-      if (j == 0) xt[(4 * u + 2 * L + (g & 1)) * 2 + (g >> 1)] = d;
+      if (j == 0) xt[(4 * u + 2 * L + (g & 1)) * 2 + (g >> 1)] = -d;
     }
   }
   __syncthreads();
@@ -431,7 +432,6 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
   // ---- 5. the blocks, as one flat sequence of rounds: round q of the wave
   // is line group r = q % NR of its block gw + (q / NR) W, and the ring's
   // refills during round q load round q + 1
-  const f32x4_f4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
   const int ssh = 16 * (g & 1);
   const int rd_q = 2 * (g & 1) + (g >> 1);
   // results: a buffer over y, so that the rows past n of the last block are
@@ -462,7 +462,8 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
       const int u = r * UD + ud;
       const i32x8_f4 a00 = read_a(u, 0, 0), a01 = read_a(u, 0, 1);
       const i32x8_f4 a10 = read_a(u, 1, 0), a11 = read_a(u, 1, 1);
-      // the all-ones sums of the lane's group (4u + 2L + g%2) and digits
+      // -X of the lane's group (4u + 2L + g%2) and digits: the chains'
+      // starting values
       const f32x4_f4 x0 = xt[(4 * u + (g & 1)) * 2 + (g >> 1)], x1 = xt[(4 * u + 2 + (g & 1)) * 2 + (g >> 1)];
 #pragma unroll
       for (int t = 0; t < T; ++t) {
@@ -477,12 +478,12 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
         f4_codes(c1, b10, b11);
         const u32x2 sv = *reinterpret_cast<const u32x2 *>(sct + (16 * t + j) * gbytes + 8 * u);
         const uint32_t s0 = sv[0], s1 = sv[1];
-        f32x4_f4 d0 = mfma_f4(a00, b00, zero, sa);
-        f32x4_f4 d1 = mfma_f4(a10, b10, zero, sa);
+        f32x4_f4 d0 = mfma_f4(a00, b00, x0, sa);
+        f32x4_f4 d1 = mfma_f4(a10, b10, x1, sa);
         d0 = mfma_f4(a01, b01, d0, sa);
         d1 = mfma_f4(a11, b11, d1, sa);
-        const float z0 = ((d0[0] - x0[0]) + (d0[1] - x0[1])) + ((d0[2] - x0[2]) + (d0[3] - x0[3]));
-        const float z1 = ((d1[0] - x1[0]) + (d1[1] - x1[1])) + ((d1[2] - x1[2]) + (d1[3] - x1[3]));
+        const float z0 = (d0[0] + d0[1]) + (d0[2] + d0[3]);
+        const float z1 = (d1[0] + d1[1]) + (d1[2] + d1[3]);
         acc[t] = __builtin_fmaf(f16_to_f32((uint16_t)(s0 >> ssh)), z0, acc[t]);
         acc[t] = __builtin_fmaf(f16_to_f32((uint16_t)(s1 >> ssh)), z1, acc[t]);
         // refill the slot only once all its registers are consumed, and
