@@ -426,7 +426,7 @@ def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream, head_copies, c4)
         s4 = bits_dev(c4["sign_bits"], torch.bfloat16)
         xr = tq.hadamard_signed(x4, s4, out_dtype=torch.float16)
         y4 = torch.empty((1, n4), dtype=torch.float32, device=xr.device)
-        mean = event_timed(torch, lambda i: tq.gemv_rowsplit(cps[i % 2], fmt4, n4, k4, xr, out=y4), 20)
+        mean = event_timed(torch, lambda i: tq.gemv_rowsplit(cps[i % 2], fmt4, n4, k4, xr, out=y4), 100)
         byts = pbytes + 2 * k4 + 4 * n4
         res["cfg4_head_gemv_alone_b1"] = {"mean_launch_us": round(mean * 1e6, 3),
                                           "gbs": round(byts / mean / 1e9, 1),
@@ -436,7 +436,7 @@ def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream, head_copies, c4)
         tok = torch.empty(1, dtype=torch.int32, device=xr.device)
         hmean = event_timed(torch, lambda i: tq.head_argmax(cps[i % 2], fmt4, n4, k4, x4, gnorm,
                                                              1e-6, s4, work, logits=y4[0], token=tok),
-                            20)
+                            100)
         hbytes = pbytes + 3 * 2 * k4 + 4 * n4 + 4
         res["cfg4_head_greedy_one_launch"] = {"mean_launch_us": round(hmean * 1e6, 3),
                                               "gbs": round(hbytes / hmean / 1e9, 1),
