@@ -92,9 +92,17 @@ __global__ __launch_bounds__(64 * W) void gemv_quads_kernel(Planes p, const void
   __shared__ uint32_t lut[256];
   // per-wave activation staging (prologue), then the per-wave partial sums
   // [row-quad][wave][g*16 + j*4 + e] (epilogue)
-  constexpr int XST = W * SB * 512 * 2, RED = RQMAX * W * 16 * NG * 4;
+  // Activation staging: per wave SB rows of XROW words, a row being the
+  // slot's 512 activations as four groups of 64 words (128 activations),
+  // group g at word XGRP*g.  PTQ1_0 pads the groups to 80 words and the rows
+  // to 324 (4 mod 64), so that the 64 lanes' chunk reads (words 15q + t and
+  // 60 + q of a group, for their row j, group and quarter q) meet 64
+  // different banks; unpadded, the 16 lanes of one quarter share a bank.
+  constexpr int XGRP = FMT == FMT_PTQ1 ? 80 : 64;
+  constexpr int XROW = FMT == FMT_PTQ1 ? 324 : 256;
+  constexpr int XST = W * SB * XROW * 4, RED = RQMAX * W * 16 * NG * 4;
   __shared__ __attribute__((aligned(16))) uint8_t lds[XST > RED ? XST : RED];
-  uint16_t(*xst)[SB][512] = reinterpret_cast<uint16_t(*)[SB][512]>(lds);
+  uint32_t *xst = reinterpret_cast<uint32_t *>(lds);
   float *red = reinterpret_cast<float *>(lds);
 
   const int lane = threadIdx.x & 63;
@@ -222,12 +230,13 @@ __global__ __launch_bounds__(64 * W) void gemv_quads_kernel(Planes p, const void
           h[t] = ok ? (uint32_t)f32_to_f16(v[2 * t]) | ((uint32_t)f32_to_f16(v[2 * t + 1]) << 16)
                     : 0u;
       }
-      *reinterpret_cast<u32x4 *>(&xst[wave][bb][8 * lane]) = (u32x4){h[0], h[1], h[2], h[3]};
+      *reinterpret_cast<u32x4 *>(xst + (wave * SB + bb) * XROW + (lane >> 4) * XGRP + 4 * (lane & 15)) =
+          (u32x4){h[0], h[1], h[2], h[3]};
     }
     // this lane's chunk blk of batch row 4g + j.  PTQ1_0: 30 base trits at
     // 128*(blk/4) + 30*(blk%4), 2 high trits at 128*(blk/4) + 120 + 2*(blk%4);
     // PQ2_0: 32 consecutive weights at 32*blk
-    const uint32_t *src = reinterpret_cast<const uint32_t *>(&xst[wave][BT == 1 ? 0 : j][128 * (blk >> 2)]);
+    const uint32_t *src = xst + (wave * SB + (BT == 1 ? 0 : j)) * XROW + (blk >> 2) * XGRP;
     uint32_t w[16];
     if constexpr (FMT == FMT_PTQ1) {
 #pragma unroll
