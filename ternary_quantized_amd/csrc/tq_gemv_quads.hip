@@ -198,6 +198,12 @@ __global__ __launch_bounds__(64 * W) void gemv_quads_kernel(Planes p, const void
     for (int s = 0; s < S; ++s) load_step(rr, s, ring[s]);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // ---- the digit table (PTQ1_0), built while the loads are in flight
+  for (int v = threadIdx.x; v < (FMT == FMT_PTQ1 ? 256 : 0); v += blockDim.x) {
+    uint32_t a = (uint32_t)v, w = 0;
+    for (int i = 0; i < 5; ++i) { w |= (a % 3u) << (2 * i); a /= 3u; }
+    lut[v] = w;
+  }
 #pragma unroll
   for (int g = 0; g < NG; ++g)
 #pragma unroll
@@ -279,13 +285,7 @@ __global__ __launch_bounds__(64 * W) void gemv_quads_kernel(Planes p, const void
     for (int s = 0; s < S; ++s) load_step(rr, s, ring[r * S + s]);
   }
 
-  // ---- the digit table (PTQ1_0)
-  for (int v = threadIdx.x; v < (FMT == FMT_PTQ1 ? 256 : 0); v += blockDim.x) {
-    uint32_t a = (uint32_t)v, w = 0;
-    for (int i = 0; i < 5; ++i) { w |= (a % 3u) << (2 * i); a /= 3u; }
-    lut[v] = w;
-  }
-  __syncthreads();
+  __syncthreads();  // the digit table and every wave's staging are written
 
   uint32_t magic_v = 0x64006400u;
   asm volatile("" : "+v"(magic_v));
@@ -358,8 +358,9 @@ __global__ __launch_bounds__(64 * W) void gemv_quads_kernel(Planes p, const void
           a1 = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, xp[0][s][m + 1]),
                                                   __builtin_bit_cast(half4_t, T[m + 1]), a1, 0, 0, 0);
         }
+        // (one batch row: only row 0 of the 4x4 products is not zero)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) yacc[0][r][e] += sc * (a0[e] + a1[e]);
+        for (int e = 0; e < (BT == 1 ? 1 : 4); ++e) yacc[0][r][e] += sc * (a0[e] + a1[e]);
       } else {
         // one chain per group of four batch rows (registers are short)
         floatx4 a[NG];
@@ -398,7 +399,7 @@ __global__ __launch_bounds__(64 * W) void gemv_quads_kernel(Planes p, const void
   int rq0 = 0;
   for (; rq0 + RR < sh.rq; rq0 += RR) do_round(rq0, std::integral_constant<bool, true>{}, RR);
   // (the red buffer shares LDS with the activation staging, which every
-  // wave finished reading before the barrier after the digit table)
+  // wave finished reading before the barrier after the staging)
   do_round(rq0, std::integral_constant<bool, false>{}, sh.rq - rq0);
   __syncthreads();
 
