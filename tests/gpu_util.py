@@ -55,3 +55,13 @@ def assert_within(got, expect, bound, what):
     assert bad.size == 0, "%s: %d outputs out of bound, first at %s: got %r expect %r bound %r" % (
         what, len(bad), bad[0], got[tuple(bad[0])], expect[tuple(bad[0])], bound[tuple(bad[0])])
     return ratio
+
+
+def pq2_b1_kernel(n, k):
+    """Which kernel the library runs for a batch-1 PQ2_0 product of n rows of
+    k weights, by its shape rule: "f4", the matrix-core kernel (rows of a
+    multiple of 1024 weights up to 8192, at least 2^29 weights), else "dot",
+    the dot-product kernels."""
+    if k >= 1024 and k % 1024 == 0 and k <= 8192 and n * k >= 1 << 29:
+        return "f4"
+    return "dot"

@@ -13,7 +13,7 @@ import pytest
 import ternary_quantized_amd as tq
 import synth
 from oracle import codec, projection as P, q2g64
-from gpu_util import assert_within, dev, say, to_f64, x_dev, x_f64
+from gpu_util import assert_within, dev, pq2_b1_kernel, say, to_f64, x_dev, x_f64
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -112,11 +112,10 @@ def test_gemv_g64_multi_pass_integer_exact(n, k):
 @pytest.mark.parametrize("n,k", [(17408, 5120), (1000, 11264), (513, 2048)])
 def test_gemv_g64_equals_plane_gemv(n, k):
     """On PQ2_0 data the G64 GEMV and the plane GEMV read the same codes and
-    scales.  Where the plane GEMV runs the dot-product kernel (matrices under
-    2^29 weights, rows over 8192 weights) both do the same arithmetic in the
-    same order and the results are bit-identical; where it takes the
-    matrix-core kernel, whose sums are grouped differently, both are held to
-    the oracle's bound."""
+    scales.  Where the plane GEMV runs the dot-product kernel both do the
+    same arithmetic in the same order and the results are bit-identical;
+    where it takes the matrix-core kernel, whose sums are grouped differently,
+    both are held to the oracle's bound."""
     rng, _, _, payload = case("PQ2_0_G128", n, k, seed=n + 5 * k)
     xr = rand_x(rng, k, "f16")
     say("gemv g64 vs planes n=%d k=%d" % (n, k))
@@ -125,7 +124,7 @@ def test_gemv_g64_equals_plane_gemv(n, k):
     y1 = tq.gemv_g64(tq.expand_g64(pd, "PQ2_0_G128", n, k), n, k, xd)
     y2 = tq.gemv_rowsplit(pd, "PQ2_0_G128", n, k, xd)
     torch.cuda.synchronize()
-    if k > 8192 or n * k < 2 ** 29:
+    if pq2_b1_kernel(n, k) == "dot":
         assert torch.equal(y1, y2)
     else:
         expect, bound = P.project_payload("PQ2_0_G128", n, k, payload, x_f64(xr, "f16"))
