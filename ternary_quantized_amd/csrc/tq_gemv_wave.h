@@ -236,7 +236,7 @@ __device__ __forceinline__ float rows8_sum(const float (&v)[D], int lane, int &r
 // workgroup takes the maximum over its waves, and one 64-bit atomic maximum
 // per workgroup merges them; the last workgroup to finish writes the token.
 // y (the logits) may be null.
-template <int LAY, int A, int BQ, int D, int XD, int MODE, int WPG>
+template <int LAY, int A, int BQ, int D, int XD, int MODE, int WPG, int KS = 1>
 __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const void *__restrict__ x,
                                                              const uint16_t *__restrict__ signs,
                                                              float *__restrict__ y, StepArgs hd) {
@@ -244,6 +244,21 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   constexpr bool HEAD = MODE == MODE_HEAD;
   constexpr int NB = 4 * A + BQ;  // 1024-element blocks in a row = 16-weight dwords per lane
   constexpr int NP = A + BQ;      // pieces per lane
+  // K split (KS = 2, long rows): the waves of a workgroup pair up, waves 2m
+  // and 2m+1 sharing their rows.  Half 0 takes the first A/2 4096-weight
+  // pieces of every row, half 1 the other A/2 and the 1024-weight pieces
+  // (half 0 holds phantom copies of those: no bytes, zero activations).
+  // Half 1 leaves its row sums in LDS; half 0 adds them to its own, in that
+  // order, and writes the row.  Each wave then holds half the row's
+  // activation pairs, so two waves fit a SIMD where one did.
+  static_assert(KS == 1 || (KS == 2 && A % 2 == 0 && MODE != MODE_HEAD && WPG % 2 == 0),
+                "the K split serves the GEMV (transform fused or not) with an even count of 4096-weight pieces");
+  constexpr int AW = A / KS;        // 4096-weight pieces per wave
+  constexpr int NBW = 4 * AW + BQ;  // code dwords (and activation dwords) per lane of a wave
+  constexpr int NPW = AW + BQ;      // pieces per wave
+  constexpr int KPASS = 8;          // passes per wave pair the row-sum slots hold (K split)
+  __shared__ float kpart[KS == 2 ? WPG / 2 : 1][KS == 2 ? KPASS : 1][8];
+  __shared__ uint32_t kready[KS == 2 ? WPG / 2 : 1];
   // Activation pairs: dword s of lane l (16 weights, pairs (4B, 4B+2) and
   // (4B+1, 4B+3) as dword_codes orders them) is held by quads (2s)*64 + l
   // (pairs 0-3) and (2s+1)*64 + l (pairs 4-7).  Dword s
@@ -260,8 +275,11 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   // the wave index is made explicitly uniform so that row offsets live in
   // scalar registers and every load is (scalar row base + lane offset)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t gw = (int64_t)blockIdx.x * WPG + wave;
-  const int64_t W = (int64_t)gridDim.x * WPG;
+  const int kh = KS == 2 ? (wave & 1) : 0;  // the wave's half of every row
+  const bool kmain = KS == 1 || kh == 1;    // the wave holds the 1024-weight pieces
+  // row streams: one per wave, or one per wave pair
+  const int64_t gw = KS == 2 ? (int64_t)blockIdx.x * (WPG / 2) + (wave >> 1) : (int64_t)blockIdx.x * WPG + wave;
+  const int64_t W = (int64_t)gridDim.x * (WPG / KS);
   const bool stager = wave < NB;
 
   // ---- rows: in pass q wave gw takes the D consecutive rows (q*W + gw)*D
@@ -292,7 +310,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   const int gq_blk = lane >> 2;
   const int gq_off = 18 * gq_blk + 4 * (lane & 3) - 2 * (gq_blk & 1);
   const uint32_t gq_sel = (gq_blk & 1) ? 0x07060504u : 0x05040302u;
-  auto load_row = [&](int row, int fb, WRaw<LAY, A, BQ> &r) {
+  auto load_row = [&](int row, int fb, WRaw<LAY, AW, BQ> &r) {
     const int rr = row < n32 ? row : fb;
     // the row's bytes as a buffer: the row address stays in scalar
     // registers and each load adds only the lane's offset (a streaming load
@@ -302,46 +320,51 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
     if constexpr (LAY == LAY_PLANES) {
       const uint16_t *rs = p.scale + (int64_t)rr * p.groups;
 #pragma unroll
-      for (int i = 0; i < A; ++i) {
-        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane + 1024 * i, 0, CPOL_NT);
+      for (int i = 0; i < AW; ++i) {
+        const int gi = i + AW * kh;  // the piece in the row
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rb, 16 * lane + 1024 * gi, 0, CPOL_NT);
         r.w[4 * i] = t[0]; r.w[4 * i + 1] = t[1]; r.w[4 * i + 2] = t[2]; r.w[4 * i + 3] = t[3];
-        r.s[i] = rs[q0 + 32 * i];
+        r.s[i] = rs[q0 + 32 * gi];
       }
+      // (phantoms read past the buffer's end: zero, and no bytes move)
 #pragma unroll
       for (int j = 0; j < BQ; ++j) {
-        r.w[4 * A + j] = __builtin_amdgcn_raw_buffer_load_b32(rb, 1024 * A + 4 * lane + 256 * j, 0, CPOL_NT);
-        r.s[A + j] = rs[q1 + 8 * j];
+        r.w[4 * AW + j] = __builtin_amdgcn_raw_buffer_load_b32(
+            rb, kmain ? 1024 * A + 4 * lane + 256 * j : 0x7FFFFFF0, 0, CPOL_NT);
+        r.s[AW + j] = rs[q1 + 8 * j];
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < A; ++i) {
-        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rb, gb_off + 1152 * i, 0, CPOL_NT);
+      for (int i = 0; i < AW; ++i) {
+        const int gi = i + AW * kh;
+        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rb, gb_off + 1152 * gi, 0, CPOL_NT);
         r.w[5 * i] = t[0]; r.w[5 * i + 1] = t[1]; r.w[5 * i + 2] = t[2]; r.w[5 * i + 3] = t[3];
-        r.w[5 * i + 4] = __builtin_amdgcn_raw_buffer_load_b32(rb, gb_off + 1152 * i + 16, 0, CPOL_NT);
+        r.w[5 * i + 4] = __builtin_amdgcn_raw_buffer_load_b32(rb, gb_off + 1152 * gi + 16, 0, CPOL_NT);
       }
 #pragma unroll
       for (int j = 0; j < BQ; ++j) {
-        const int o = 1152 * A + 288 * j;
+        const int o = kmain ? 1152 * A + 288 * j : 0x7FFFF000;
         const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(rb, o + gq_off, 0, CPOL_NT);
-        r.w[5 * A + 2 * j] = t[0]; r.w[5 * A + 2 * j + 1] = t[1];
+        r.w[5 * AW + 2 * j] = t[0]; r.w[5 * AW + 2 * j + 1] = t[1];
         r.s[j] = __builtin_amdgcn_raw_buffer_load_b16(rb, o + 18 * gq_blk, 0, CPOL_NT);
       }
     }
   };
   // codes dword q of piece pc, and the piece's scale bits, of a loaded row
-  auto codes_of = [&](const WRaw<LAY, A, BQ> &r, int pc, int q) -> uint32_t {
+  auto codes_of = [&](const WRaw<LAY, AW, BQ> &r, int pc, int q) -> uint32_t {
     if constexpr (LAY == LAY_PLANES) {
-      return r.w[pc < A ? 4 * pc + q : 4 * A + (pc - A)];
+      return r.w[pc < AW ? 4 * pc + q : 4 * AW + (pc - AW)];
     } else {
-      if (pc < A) return __builtin_amdgcn_perm(r.w[5 * pc + q + 1], r.w[5 * pc + q], gb_sel);
-      return __builtin_amdgcn_perm(r.w[5 * A + 2 * (pc - A) + 1], r.w[5 * A + 2 * (pc - A)], gq_sel);
+      if (pc < AW) return __builtin_amdgcn_perm(r.w[5 * pc + q + 1], r.w[5 * pc + q], gb_sel);
+      return __builtin_amdgcn_perm(r.w[5 * AW + 2 * (pc - AW) + 1], r.w[5 * AW + 2 * (pc - AW)], gq_sel);
     }
   };
-  auto scale_of = [&](const WRaw<LAY, A, BQ> &r, int pc) -> uint16_t {
-    if constexpr (LAY == LAY_PLANES) return (uint16_t)r.s[pc];
-    else return pc < A ? (uint16_t)(r.w[5 * pc] >> gb_sh) : (uint16_t)r.s[pc - A];
+  // (a phantom piece's scale is zero)
+  auto scale_of = [&](const WRaw<LAY, AW, BQ> &r, int pc) -> uint16_t {
+    if constexpr (LAY == LAY_PLANES) return (KS == 1 || kmain || pc < AW) ? (uint16_t)r.s[pc] : (uint16_t)0;
+    else return pc < AW ? (uint16_t)(r.w[5 * pc] >> gb_sh) : (uint16_t)r.s[pc - AW];
   };
-  WRaw<LAY, A, BQ> ring[D];
+  WRaw<LAY, AW, BQ> ring[D];
   const int gw32 = (int)gw, W32 = (int)W;
   const int first = gw32 * D < n32 ? gw32 * D : n32 - 1;
   auto load_first = [&]() {
@@ -372,6 +395,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
     staged = 0;
     sq_posted = 0;
   }
+  if (KS == 2 && threadIdx.x < WPG / 2) kready[threadIdx.x] = 0;
   if (stager) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -530,14 +554,17 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
 
   // ---- 4. the lane's activation pairs (read before the staging waves
   // request their rows, which may stall at issue)
-  half2_t xp[NB][8];
+  half2_t xp[NBW][8];
 #pragma unroll
-  for (int s = 0; s < NB; ++s) {
-    const u32x4 a = xq[(2 * s) * 64 + lane], b = xq[(2 * s + 1) * 64 + lane];
+  for (int s = 0; s < NBW; ++s) {
+    // the dword in the row's staging order, and whether it is a phantom
+    const int sg = s < 4 * AW ? s + 4 * AW * kh : 4 * A + (s - 4 * AW);
+    const bool ph = s >= 4 * AW && !kmain;
+    const u32x4 a = xq[(2 * sg) * 64 + lane], b = xq[(2 * sg + 1) * 64 + lane];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      xp[s][k] = bits_h2(a[k]);
-      xp[s][4 + k] = bits_h2(b[k]);
+      xp[s][k] = bits_h2(ph ? 0u : a[k]);
+      xp[s][4 + k] = bits_h2(ph ? 0u : b[k]);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -548,8 +575,8 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   // in four accumulators (pair e feeds accumulator e % 4; the first product
   // of each starts from 0 instead of a zeroed register)
   auto piece_cx = [&](const uint32_t (&cw)[4], int pc) -> float {
-    const int nd = pc < A ? 4 : 1;
-    const int d0 = pc < A ? 4 * pc : 4 * A + (pc - A);
+    const int nd = pc < AW ? 4 : 1;
+    const int d0 = pc < AW ? 4 * pc : 4 * AW + (pc - AW);
     float a[4];
 #pragma unroll
     for (int q = 0; q < nd; ++q) {
@@ -568,16 +595,17 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   // piece whose weights are all zero gives cx == xs bit for bit and adds
   // exactly nothing: rounding error arises only in pieces that hold a
   // nonzero weight, and an all-zero row is exactly 0 at any scale.
-  float xs[NP];
+  float xs[NPW];
   {
     const uint32_t ones[4] = {0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u};
 #pragma unroll
-    for (int pc = 0; pc < NP; ++pc) xs[pc] = piece_cx(ones, pc);
+    for (int pc = 0; pc < NPW; ++pc) xs[pc] = piece_cx(ones, pc);
   }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- 5. passes of D rows
   unsigned long long best = 0;  // HEAD: the lane's largest key (0 is below every logit)
+  int kpass = 0;                // K split: passes done
   auto do_pass = [&](int base, auto refill) {
     float part[D];
 #pragma unroll
@@ -585,8 +613,8 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
       // sum over the lane's pieces of s * (sum code*x' - xs)
       float acc = 0.0f;
 #pragma unroll
-      for (int pc = 0; pc < NP; ++pc) {
-        const int nd = pc < A ? 4 : 1;
+      for (int pc = 0; pc < NPW; ++pc) {
+        const int nd = pc < AW ? 4 : 1;
         uint32_t cw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int q = 0; q < nd; ++q) cw[q] = codes_of(ring[d], pc, q);
@@ -600,7 +628,27 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
     }
     int r;
     const float tot = rows8_sum<D>(part, lane, r);
-    if ((lane & 7) == 7 && r < D && base + r < n32) {
+    if constexpr (KS == 2) {
+      // half 1 posts its row sums; half 0 waits for them (a bounded wait:
+      // half 1 posts once per pass on every path) and writes the rows
+      float(&slot)[8] = kpart[wave >> 1][kpass & (KPASS - 1)];
+      if (kh == 1) {
+        if ((lane & 7) == 7 && r < D) slot[r] = tot;
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        if (lane == 0)
+          __hip_atomic_fetch_add(&kready[wave >> 1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+          const uint32_t done = __builtin_amdgcn_readfirstlane(
+              __hip_atomic_load(&kready[wave >> 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+          if (done > (uint32_t)kpass) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
+        if ((lane & 7) == 7 && r < D && base + r < n32) y[base + r] = tot + slot[r];
+      }
+      ++kpass;
+    } else if ((lane & 7) == 7 && r < D && base + r < n32) {
       if constexpr (HEAD) {
         if (y) y[base + r] = tot;
         const unsigned long long key = greedy_key(tot, (uint32_t)(base + r));
@@ -651,9 +699,54 @@ static hipError_t gemv_wave_launch(const Planes &p, const void *x, const uint16_
 // row their slot already holds.  Workgroup size by register need: three
 // waves per SIMD up to k = 5120 (WPG 12), two up to k = 7168 (WPG 8), one
 // beyond (WPG 4).
-template <int LAY, int A, int BQ, int D, int XD, int MODE, int WPG>
+template <int LAY, int A, int BQ, int D, int XD, int MODE, int WPG, int KS = 1>
 static const void *gemv_wave_ptr() {
-  return reinterpret_cast<const void *>(gemv_wave_kernel<LAY, A, BQ, D, XD, MODE, WPG>);
+  return reinterpret_cast<const void *>(gemv_wave_kernel<LAY, A, BQ, D, XD, MODE, WPG, KS>);
+}
+
+// The K split for long rows (planes GEMV with four 4096-weight pieces, k =
+// 16384 or 17408): eight waves, four pairs, per workgroup, so that two
+// waves share a SIMD; the same row split as below over pairs, with at most
+// eight passes a pair (the row-sum slots).  The fused transform needs k <=
+// 11264, so the one-launch step never meets this form and keeps the
+// two-launch result bit for bit.  done = false: no depth fits.
+template <int LAY, int A, int BQ, int XD, int MODE>
+static hipError_t gemv_wave_go_ks2(const Planes &p, const void *x, const uint16_t *signs, float *y,
+                                   const StepArgs &hd, hipStream_t st, bool &done) {
+  constexpr int WPG = 8, PAIRS = WPG / 2;
+  const int depth[2] = {4, 5};
+  const void *kerns[2] = {gemv_wave_ptr<LAY, A, BQ, 4, XD, MODE, WPG, 2>(),
+                          gemv_wave_ptr<LAY, A, BQ, 5, XD, MODE, WPG, 2>()};
+  const int cus = device_cus();
+  int best = -1;
+  int64_t best_rows = 0, best_wgs = 0;
+  for (int i = 0; i < 2; ++i) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kerns[i], 64 * WPG, 0) != hipSuccess ||
+        per_cu < 1)
+      continue;
+    const int64_t D = depth[i];
+    const int64_t slots = (int64_t)PAIRS * cus * per_cu;
+    const int64_t passes = (p.n + slots * D - 1) / (slots * D);
+    if (passes > 8) continue;
+    const int64_t pairs = (p.n + D * passes - 1) / (D * passes);
+    const int64_t wgs = (pairs + PAIRS - 1) / PAIRS;
+    const int64_t rows_cu = ((wgs + cus - 1) / cus) * PAIRS * D * passes;
+    if (best < 0 || rows_cu <= best_rows) {
+      best = i;
+      best_rows = rows_cu;
+      best_wgs = wgs;
+    }
+  }
+  done = best >= 0;
+  if (!done) return hipSuccess;
+  if (depth[best] == 4)
+    hipLaunchKernelGGL((gemv_wave_kernel<LAY, A, BQ, 4, XD, MODE, WPG, 2>), dim3((unsigned)best_wgs),
+                       dim3(64 * WPG), 0, st, p, x, signs, y, hd);
+  else
+    hipLaunchKernelGGL((gemv_wave_kernel<LAY, A, BQ, 5, XD, MODE, WPG, 2>), dim3((unsigned)best_wgs),
+                       dim3(64 * WPG), 0, st, p, x, signs, y, hd);
+  return hipGetLastError();
 }
 
 template <int LAY, int A, int BQ, int XD, int MODE>
@@ -661,6 +754,14 @@ static hipError_t gemv_wave_go(const Planes &p, const void *x, const uint16_t *s
                                hipStream_t st, const StepArgs &hd = StepArgs{}) {
   constexpr int NBK = 4 * A + BQ;
   constexpr int WPG = NBK <= 5 ? 12 : NBK <= 7 ? 8 : 4;
+  // (measured: 10.2 against 10.6 us at 5120 x 17408 and 9.1 against 9.6 at
+  // 5120 x 16384; slower at k = 11264, where the halves hold 4096 and 7168
+  // weights, and no faster on the G64 stream)
+  if constexpr (LAY == LAY_PLANES && MODE == MODE_GEMV && A == 4) {
+    bool done = false;
+    const hipError_t e = gemv_wave_go_ks2<LAY, A, BQ, XD, MODE>(p, x, signs, y, hd, st, done);
+    if (done) return e;
+  }
   // ring depths tried: 4, 6, 8; the G64 stream also 5 (its long rows run
   // one wave per SIMD, where 5 rows per wave fill the chip at k = 17408)
   constexpr int ND = LAY == LAY_G64 ? 4 : 3;

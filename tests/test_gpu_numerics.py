@@ -102,10 +102,14 @@ def check_rows(got, payload, k, xrot64, zero_rows, what):
 
 
 KS = [5120, 11264]
+# the GEMV alone also at the rows of four 4096-weight pieces, which it
+# splits over a pair of waves (half the pieces each, the 1024-weight piece
+# with the second half)
+KS_PLAIN = KS + [16384, 17408]
 XKINDS = ["normal", "small", "mixed"]
 
 
-@pytest.mark.parametrize("k", KS)
+@pytest.mark.parametrize("k", KS_PLAIN)
 @pytest.mark.parametrize("xkind", XKINDS)
 def test_gemv_rowsplit_hard_rows(k, xkind):
     rng = np.random.default_rng(k + len(xkind))
