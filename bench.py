@@ -388,6 +388,19 @@ def bench_secondary(torch, tq, synth, to_dev, bits_dev, stream, head_copies, c4)
                                        "expand_us": round(emean * 1e6, 2),
                                        "expand_gbs": round((p3.size + gbytes) / emean / 1e9, 1)}
         del gcps
+        # the same trits as PQ2_0 planes (the PQ2_0 model's down projection),
+        # batch 1: the wave GEMV with each row split over a pair of waves
+        pq = tq.pack_rowsplit("PQ2_0_G128", c3["trits"], c3["scale_bits"])
+        ncq = copies_for(pq.size)
+        cpq = [to_dev(pq)]
+        cpq += [cpq[0].clone() for _ in range(ncq - 1)]
+        mean = event_timed(torch, lambda i: tq.gemv_rowsplit(cpq[i % ncq], "PQ2_0_G128", n3, k3, xr,
+                                                              out=yb), 4 * ncq)
+        byts = pq.size + 2 * k3 + 4 * n3
+        res["cfg3_shape_pq2_b1"] = {"bytes": int(pq.size), "mean_launch_us": round(mean * 1e6, 3),
+                                    "gbs": round(byts / mean / 1e9, 1),
+                                    "frac_hbm": round(byts / mean / 1e9 / HBM_PEAK_GBS, 4)}
+        del cpq
         torch.cuda.empty_cache()
 
         # GatedDeltaNet output projection N=5120 K=6144 (48 value heads of 128,
