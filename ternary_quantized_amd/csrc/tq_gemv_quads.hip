@@ -380,7 +380,9 @@ __global__ __launch_bounds__(64 * W) void gemv_quads_kernel(Planes p, const void
 #pragma unroll
           for (int e = 0; e < 4; ++e) yacc[g][r][e] += sc * a[g][e];
       }
-      __builtin_amdgcn_sched_barrier(0);
+      // the step's refill stays here; arithmetic, matrix and LDS work may
+      // move across steps (mask: everything but the global loads)
+      __builtin_amdgcn_sched_barrier(0x18F);
     }
     // per row-quad: sum over the wave's blocks, stash per wave
 #pragma unroll
