@@ -281,6 +281,26 @@ def test_gemv_batch1_multi_pass_integer_exact(n, k):
     assert np.array_equal(yf.cpu().numpy(), expect)
 
 
+def test_gemv_rows_of_four_pieces_past_the_pair_split():
+    """Rows of four 4096-weight pieces run split over wave pairs while a
+    pair needs at most eight passes; 41000 rows at k = 16384 need nine, so
+    the launch falls back to one wave per row.  Integer data (scales 1.0,
+    integer activations) make each row exact; a spread sample of rows,
+    the first and last included, is checked against integer arithmetic."""
+    n, k = 41000, 16384
+    rng = np.random.default_rng(n + k)
+    trits = synth.trits_uniform(rng, n, k)
+    sb = np.full((n, k // 128), 0x3C00, np.uint16)
+    payload = tq.pack_rowsplit("PQ2_0_G128", trits, sb)
+    xi = rng.integers(-8, 9, size=(1, k)).astype(np.float32)
+    say("gemv pair-split fallback n=%d k=%d" % (n, k))
+    y = tq.gemv_rowsplit(dev(torch, payload), "PQ2_0_G128", n, k, x_dev(torch, xi, "f32"))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, n, 97), np.arange(n - 40, n)]))
+    expect = (trits[rows].astype(np.int64) @ xi[0].astype(np.int64)).astype(np.float32)
+    assert np.array_equal(y.cpu().numpy()[0, rows], expect)
+
+
 @pytest.mark.parametrize("fmt", ["PQ2_0_G128", "PTQ1_0_G128"])
 def test_gemv_non_ternary_codes_follow_decode_arithmetic(fmt):
     n, k = 40, 1024
