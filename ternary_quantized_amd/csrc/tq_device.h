@@ -198,16 +198,23 @@ __device__ __forceinline__ void wht_regs(float v[16]) {
   }
 }
 
+// The wave's scratch holds the block as four quarters of 256 floats, each
+// followed by 16 words of padding: in the strided transpose the lanes l,
+// l+16, l+32 and l+48 read and write element 16i + l%16 of quarter l/16,
+// which without the padding fall on one bank.
+constexpr int WHT_SCRATCH = 1024 + 3 * 16;
+
 __device__ __forceinline__ void wht1024_wave(float v[16], int lane, float *sc) {
+  const int qp = 16 * (lane >> 4);  // the padding before the lane's quarter
   wht_regs<1, 8>(v);
   {
-    u32x4 *w = reinterpret_cast<u32x4 *>(sc + 16 * lane);
+    u32x4 *w = reinterpret_cast<u32x4 *>(sc + 16 * lane + qp);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       w[j] = (u32x4){__float_as_uint(v[4 * j]), __float_as_uint(v[4 * j + 1]),
                      __float_as_uint(v[4 * j + 2]), __float_as_uint(v[4 * j + 3])};
   }
-  const int t1 = (lane & 15) + 256 * (lane >> 4);
+  const int t1 = (lane & 15) + 256 * (lane >> 4) + qp;
 #pragma unroll
   for (int i = 0; i < 16; ++i) v[i] = sc[t1 + 16 * i];
   wht_regs<1, 8>(v);
@@ -215,7 +222,7 @@ __device__ __forceinline__ void wht1024_wave(float v[16], int lane, float *sc) {
   for (int i = 0; i < 16; ++i) sc[t1 + 16 * i] = v[i];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    const u32x4 r = *reinterpret_cast<const u32x4 *>(sc + 4 * lane + 256 * g);
+    const u32x4 r = *reinterpret_cast<const u32x4 *>(sc + 4 * lane + 272 * g);
 #pragma unroll
     for (int j = 0; j < 4; ++j) v[4 * g + j] = __uint_as_float(r[j]);
   }

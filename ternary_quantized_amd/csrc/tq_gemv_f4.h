@@ -296,7 +296,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_f4_kernel(Planes p, const void 
 #pragma unroll
       for (int q = 0; q < 16; ++q) v[q] = apply_sign(v[q], (uint16_t)(sw[q >> 1] >> (16 * (q & 1))));
     }
-    if (tw) wht1024_wave(v, lane, reinterpret_cast<float *>(tab) + 1024 * wave);
+    if (tw) wht1024_wave(v, lane, reinterpret_cast<float *>(tab) + WHT_SCRATCH * wave);
     float post = 0.03125f;
     if constexpr (HEAD) {
       sq = f4_wave_sum(sq);

@@ -270,7 +270,7 @@ __global__ __launch_bounds__(64 * WPG) void gemv_wave_kernel(Planes p, const voi
   __shared__ float sq_part[HEAD ? WPG : 1];
   __shared__ unsigned long long wbest[HEAD ? WPG : 1];
   // the transform's per-wave scratch (staging waves only)
-  __shared__ __attribute__((aligned(16))) float wsc[FUSED ? (NB < WPG ? NB : WPG) : 1][1024];
+  __shared__ __attribute__((aligned(16))) float wsc[FUSED ? (NB < WPG ? NB : WPG) : 1][WHT_SCRATCH];
   const int lane = threadIdx.x & 63;
   // the wave index is made explicitly uniform so that row offsets live in
   // scalar registers and every load is (scalar row base + lane offset)

@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void hadamard_kernel(
     const void *x, int64_t ldx, int64_t rows, int64_t nblocks,
     const uint16_t *__restrict__ signs, int inverse, void *y, int64_t ldy,
     int tiles, int groups, int head_dim) {
-  __shared__ __attribute__((aligned(16))) float scratch[4][1024];
+  __shared__ __attribute__((aligned(16))) float scratch[4][WHT_SCRATCH];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t item = (int64_t)blockIdx.x * 4 + wave;
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void embed_kernel(Planes p, const int32_t *__r
                                                     const uint16_t *__restrict__ signs,
                                                     float *__restrict__ out, int64_t ldo,
                                                     int32_t *err_word) {
-  __shared__ __attribute__((aligned(16))) float scratch[4][1024];
+  __shared__ __attribute__((aligned(16))) float scratch[4][WHT_SCRATCH];
   const int lane = threadIdx.x & 63;
   const int64_t nblocks = p.k / 1024;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
